@@ -1,0 +1,19 @@
+"""CPU oracle for group-wise asymmetric int4 weight-only quantization and
+the W4A16 linear layer.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
+execute this package: only the test suite, the smoke check and the CPU
+baseline leg of the benchmark use it. It shares no code with the HIP
+library and imports nothing from it.
+"""
+from .ref import (  # noqa: F401
+    GROUP_SIZES,
+    bf16_bits_to_f32,
+    f32_to_bf16_bits,
+    quantize_ref,
+    unpack_codes_ref,
+    dequant_ref,
+    linear_ref,
+    linear_rows_ref,
+    rel_frobenius,
+)

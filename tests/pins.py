@@ -1,0 +1,239 @@
+"""Checks that pin the oracle to facts outside itself (brute force, exact
+reconstruction, invariants, hand-derived fixtures). Each check takes the
+oracle's functions as arguments so the same checks can be run against
+deliberately broken copies (see test_oracle_mutants.py)."""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def f32_from_bf16(bits):
+    """Test-side bf16 decode through torch (independent of the oracle)."""
+    t = torch.from_numpy(np.asarray(bits, dtype=np.uint16).astype(np.int16))
+    return t.view(torch.bfloat16).to(torch.float32).numpy()
+
+
+def bf16_from_float(vals):
+    t = torch.tensor(np.asarray(vals, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def unpack_test(codes):
+    """Test-side nibble unpack: element 2j is the low nibble of byte j."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    out = np.zeros((codes.shape[0], codes.shape[1] * 2), dtype=np.int64)
+    for j in range(codes.shape[1]):
+        out[:, 2 * j] = codes[:, j] % 16
+        out[:, 2 * j + 1] = codes[:, j] // 16
+    return out
+
+
+# --- pin 1: hand-derived fixtures -----------------------------------------
+
+def check_golden_halfsteps(quantize):
+    g = json.load(open(os.path.join(GOLDEN, "g32_halfsteps.json")))
+    W = bf16_from_float(g["values"]).reshape(1, -1)
+    codes, s, z = quantize(W, g["G"])
+    assert [f"{b:02x}" for b in codes[0]] == g["codes_packed_hex"], "packed codes"
+    assert f"{int(s[0, 0]):04x}" == g["scale_bits_hex"], "scale bits"
+    assert f"{int(z[0, 0]):04x}" == g["zero_bits_hex"], "zero bits"
+    assert list(unpack_test(codes)[0]) == g["codes_unpacked"], "unpacked"
+
+
+def check_golden_special(quantize):
+    g = json.load(open(os.path.join(GOLDEN, "special_groups.json")))
+    for case in g["cases"]:
+        if "values_head" in case:
+            vals = np.full(32, case["rest"], dtype=np.float32)
+            vals[:len(case["values_head"])] = case["values_head"]
+        elif "fill" in case:
+            vals = np.full(32, case["fill"], dtype=np.float32)
+        elif case["pattern"].startswith("alternate"):
+            vals = np.array([0.0, -0.0] * 16, dtype=np.float32)
+        else:
+            vals = np.zeros(32, dtype=np.float32)
+            vals[0] = -0.0
+            vals[1] = 15.0
+        W = bf16_from_float(vals).reshape(1, 32)
+        codes, s, z = quantize(W, 32)
+        assert f"{int(s[0, 0]):04x}" == case["scale_bits_hex"], case["name"]
+        assert f"{int(z[0, 0]):04x}" == case["zero_bits_hex"], case["name"]
+        if "codes_packed_hex" in case:
+            assert all(f"{b:02x}" == case["codes_packed_hex"] for b in codes[0]), case["name"]
+        if "codes_first_two" in case:
+            assert list(unpack_test(codes)[0, :2]) == case["codes_first_two"], case["name"]
+        if "codes_first" in case:
+            n = len(case["codes_first"])
+            assert list(unpack_test(codes)[0, :n]) == case["codes_first"], case["name"]
+
+
+# --- pin 2: brute force nearest code (exact rational arithmetic) -----------
+
+def brute_force_codes(W_bits, G, s_bits, z_bits):
+    """For each element pick the code q in 0..15 whose q*s + z is nearest to
+    w in exact arithmetic, ties to the even code. Uses the scale and offset
+    under test; also returns the exact quotient (w - z)/s per element."""
+    w = f32_from_bf16(W_bits).astype(np.float64)
+    s = f32_from_bf16(s_bits).astype(np.float64)
+    z = f32_from_bf16(z_bits).astype(np.float64)
+    N, K = w.shape
+    q = np.zeros((N, K), dtype=np.int64)
+    quot = np.zeros((N, K), dtype=object)
+    for n in range(N):
+        for k in range(K):
+            sv = Fraction(s[n, k // G])
+            zv = Fraction(z[n, k // G])
+            wv = Fraction(w[n, k])
+            if sv == 0:
+                q[n, k] = 0
+                quot[n, k] = None
+                continue
+            best, best_err = None, None
+            for c in range(16):
+                err = abs(wv - (c * sv + zv))
+                if best is None or err < best_err or (err == best_err and c % 2 == 0):
+                    best, best_err = c, err
+            q[n, k] = best
+            quot[n, k] = (wv - zv) / sv
+    return q, quot
+
+
+def check_brute_force(quantize, W_bits, G, tol_rel=2.0**-20):
+    """Codes equal the brute-force nearest codes except where the exact
+    quotient lies within tol_rel of a half-integer (there float32 rounding of
+    the subtraction or the quotient decides, and both neighbours are
+    acceptable). Returns the number of such boundary elements."""
+    codes, s_bits, z_bits = quantize(W_bits, G)
+    q = unpack_test(codes)
+    qb, quot = brute_force_codes(W_bits, G, s_bits, z_bits)
+    near = 0
+    for idx in zip(*np.nonzero(q != qb)):
+        t = quot[idx]
+        assert t is not None, f"code mismatch at {idx} with zero scale"
+        assert t >= 0
+        half = math.floor(t) + Fraction(1, 2)
+        # an exact tie whose float32 numerator is exact must go to even
+        w32 = np.float32(f32_from_bf16(W_bits)[idx])
+        z32 = np.float32(f32_from_bf16(z_bits)[idx[0], idx[1] // G])
+        exact_num = Fraction(float(np.float32(w32 - z32))) == Fraction(float(w32)) - Fraction(float(z32))
+        assert not (t == half and exact_num), f"exact tie at {idx} not rounded to even"
+        assert abs(t - half) <= tol_rel * max(abs(t), 1), (
+            f"code {q[idx]} != brute force {qb[idx]} at {idx}, quotient {float(t)}")
+        assert abs(int(q[idx]) - int(qb[idx])) == 1
+        near += 1
+    return near
+
+
+# --- pin 3: invariants -----------------------------------------------------
+
+def check_invariants(quantize, dequant, W_bits, G):
+    codes, s_bits, z_bits = quantize(W_bits, G)
+    N, K = W_bits.shape
+    w = f32_from_bf16(W_bits).astype(np.float64)
+    s = f32_from_bf16(s_bits).astype(np.float64)
+    z = f32_from_bf16(z_bits).astype(np.float64)
+    q = unpack_test(codes)
+    assert codes.shape == (N, K // 2) and codes.dtype == np.uint8
+    assert s_bits.shape == (N, K // G) and z_bits.shape == (N, K // G)
+    assert q.min() >= 0 and q.max() <= 15
+    wg = w.reshape(N, K // G, G)
+    qg = q.reshape(N, K // G, G)
+    # offset is the group minimum (an element of the group)
+    assert np.array_equal(z, wg.min(axis=2) + 0.0), "zero != group minimum"
+    w_hat = dequant(codes, s_bits, z_bits, G)
+    # |w_hat - w| <= s/2 elementwise (s > 0), exact round trip when s == 0
+    err = np.abs(w_hat - w).reshape(N, K // G, G)
+    pos = s > 0
+    assert np.all(err[pos] <= (s[pos] / 2.0)[:, None] * (1 + 1e-12)), "error > s/2"
+    cst = wg.max(axis=2) == wg.min(axis=2)
+    assert np.all(err[cst] == 0.0), "constant group does not round-trip"
+    assert np.all(s[cst] == 0.0)
+    # every group with s > 0 uses code 0 (at its minimum) and code 15 (at its max)
+    amin = np.argmin(wg, axis=2)
+    amax = np.argmax(wg, axis=2)
+    ii, jj = np.nonzero(pos)
+    assert np.all(qg[ii, jj, amin[ii, jj]] == 0), "minimum not coded 0"
+    assert np.all(qg[ii, jj, amax[ii, jj]] == 15), "maximum not coded 15"
+    # scale is the bf16 rounding of range/15 (within half a bf16 ulp)
+    rng = (wg.max(axis=2) - wg.min(axis=2))[pos] / 15.0
+    assert np.all(np.abs(s[pos] - rng) <= rng * 2.0**-8 + 1e-300)
+
+
+# --- pin 4: exact reconstruction and the linear -----------------------------
+
+def grid_weights(N, K, G, seed, lo_exp=-6, s_exp=-9):
+    """W[n, k] = lo[n,g] + j[n,k] * 2^s_exp with j in 0..15 and both 0 and 15
+    present in every group, so the quantizer must return exactly j, s and lo.
+    lo is a multiple of 2^s_exp (so every grid point is exact in bf16)."""
+    rng = np.random.default_rng(seed)
+    j = rng.integers(0, 16, size=(N, K // G, G))
+    j[:, :, 0] = 0
+    j[:, :, 1] = 15
+    for n in range(N):                  # shuffle the positions of 0 and 15
+        for g in range(K // G):
+            rng.shuffle(j[n, g])
+    step = 2.0 ** s_exp
+    lo = rng.integers(-(2 ** (lo_exp - s_exp)), 2 ** (lo_exp - s_exp),
+                      size=(N, K // G)) * step
+    w = lo[:, :, None] + j * step
+    bits = bf16_from_float(w.reshape(N, K))
+    assert np.array_equal(f32_from_bf16(bits).astype(np.float64), w.reshape(N, K))
+    return bits, j.reshape(N, K), lo, step
+
+
+def check_grid_exact(quantize, dequant, linear, M, N, K, G, seed, with_bias):
+    W_bits, j, lo, step = grid_weights(N, K, G, seed)
+    codes, s_bits, z_bits = quantize(W_bits, G)
+    assert np.array_equal(unpack_test(codes), j), "codes != grid indices"
+    assert np.all(f32_from_bf16(s_bits) == step), "scale != grid step"
+    assert np.array_equal(f32_from_bf16(z_bits).astype(np.float64), lo + 0.0)
+    w = f32_from_bf16(W_bits).astype(np.float64)
+    assert np.array_equal(dequant(codes, s_bits, z_bits, G), w)
+    rng = np.random.default_rng(seed + 1)
+    x_bits = bf16_from_float(rng.standard_normal((M, K)))
+    b_bits = bf16_from_float(rng.standard_normal(N)) if with_bias else None
+    y = linear(x_bits, codes, s_bits, z_bits, G, b_bits)
+    # independent reference: torch float64 matmul of the original weights
+    xt = torch.from_numpy(f32_from_bf16(x_bits).astype(np.float64))
+    yt = xt @ torch.from_numpy(w).T
+    if with_bias:
+        yt = yt + torch.from_numpy(f32_from_bf16(b_bits).astype(np.float64))
+    yt = yt.numpy()
+    assert y.shape == (M, N)
+    assert np.allclose(y, yt, rtol=1e-12, atol=1e-12), "linear != x @ W^T"
+
+
+# --- pin 5: bf16 rounding helper against torch -----------------------------
+
+def check_bf16_helper(f32_to_bf16_bits):
+    rng = np.random.default_rng(11)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        ((rng.integers(0, 0x7F7F, 5000, dtype=np.uint32) << 16) | 0x8000).view(np.float32),
+    ]).astype(np.float32)
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(f32_to_bf16_bits(x), theirs), "bf16 rounding"
+
+
+def run_all_pins(mod):
+    """Every pin against an oracle module-like object."""
+    check_bf16_helper(mod.f32_to_bf16_bits)
+    check_golden_halfsteps(mod.quantize_ref)
+    check_golden_special(mod.quantize_ref)
+    rng = np.random.default_rng(3)
+    for G in (32, 64):
+        W = bf16_from_float(rng.standard_normal((2, 2 * G)) * 0.02)
+        check_brute_force(mod.quantize_ref, W, G)
+        V = rng.standard_normal((6, 2 * G)) * 10.0 ** rng.integers(-3, 3, (6, 1))
+        V[1, :G] = 0.25
+        check_invariants(mod.quantize_ref, mod.dequant_ref, bf16_from_float(V), G)
+    check_grid_exact(mod.quantize_ref, mod.dequant_ref, mod.linear_ref,
+                     3, 24, 256, 64, seed=9, with_bias=True)

@@ -1,0 +1,58 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and check
+that the pins catch every one of them."""
+import types
+
+import pytest
+
+from oracle import ref
+from tests import pins
+
+MUTANTS = {
+    "scale_over_16": ("d / np.float32(15.0)", "d / np.float32(16.0)"),
+    "no_signed_zero_canon": ("lo = v.min(axis=2) + np.float32(0.0)", "lo = v.min(axis=2)"),
+    "zero_is_max": ("z_bits = (lo.view", "z_bits = (hi.view"),
+    "round_half_up": ("np.clip(np.rint(quot)", "np.clip(np.floor(quot + 0.5)"),
+    "truncate": ("np.clip(np.rint(quot)", "np.clip(np.trunc(quot)"),
+    "reciprocal_multiply": (
+        "quot = np.divide(num, np.where(zero_scale, np.float32(1.0), s_b),",
+        "quot = np.multiply(num, np.float32(1.0) / np.where(zero_scale, np.float32(1.0), s_b),"),
+    "scale_truncated_to_bf16": (
+        "s_bits = f32_to_bf16_bits(s32)",
+        "s_bits = (s32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)"),
+    "nibbles_swapped": (
+        "codes = (q[:, 0::2] | (q[:, 1::2] << np.uint8(4)))",
+        "codes = (q[:, 1::2] | (q[:, 0::2] << np.uint8(4)))"),
+    "dequant_drops_zero": (
+        "return q * np.repeat(s, G, axis=1) + np.repeat(z, G, axis=1)",
+        "return q * np.repeat(s, G, axis=1)"),
+    "dequant_wrong_group_index": (
+        "return q * np.repeat(s, G, axis=1) + np.repeat(z, G, axis=1)",
+        "return q * np.tile(s, (1, G)) + np.tile(z, (1, G))"),
+    "linear_reversed_k": ("y[:, n0:n1] = x @ w.T", "y[:, n0:n1] = x @ w[:, ::-1].T"),
+    "bias_sign": ("y += bf16_bits_to_f32", "y -= bf16_bits_to_f32"),
+    "zero_scale_code_15": ("q = np.where(zero_scale, 0.0, q)", "q = np.where(zero_scale, 15.0, q)"),
+    "bf16_round_half_up": (
+        "u = u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))",
+        "u = u + np.uint64(0x8000)"),
+    "range_min_min": ("hi = v.max(axis=2) + np.float32(0.0)", "hi = v.min(axis=2) + np.float32(1.0)"),
+}
+
+
+def _mutant_module(old, new):
+    src = open(ref.__file__).read()
+    assert src.count(old) == 1, f"mutation anchor not found once: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = ref.__file__
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def test_unmutated_oracle_passes_all_pins():
+    pins.run_all_pins(ref)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name):
+    mod = _mutant_module(*MUTANTS[name])
+    with pytest.raises((AssertionError, ValueError)):
+        pins.run_all_pins(mod)
