@@ -1,0 +1,162 @@
+"""Python binding of libw4a16.so: group-wise asymmetric int4 weight-only
+quantization and the W4A16 linear on MI355X (gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+torch supplies device memory and the current stream. The library must be
+built (``python -m bit_gemm_quantize_amd.build``); nothing here falls back
+to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import enum
+import os
+
+from .build import LIB_PATH
+
+__all__ = [
+    "W4Status", "W4Path", "W4Error", "GROUP_SIZES", "GEMV_MAX_M", "lib",
+    "quantize_int4_grouped", "w4a16_linear", "status_string",
+]
+
+GROUP_SIZES = (32, 64, 128)
+GEMV_MAX_M = 16
+
+
+class W4Status(enum.IntEnum):
+    OK = 0
+    ERR_NULL = 1
+    ERR_SHAPE = 2
+    ERR_GROUP = 3
+    ERR_ALIGN = 4
+    ERR_HIP = 5
+    ERR_ALIAS = 6
+    ERR_PATH = 7
+
+
+class W4Path(enum.IntEnum):
+    AUTO = 0
+    GEMV = 1
+    GEMM = 2
+
+
+class W4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+_LIB = None
+_p, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build the HIP library first "
+                "(python -m bit_gemm_quantize_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.quantize_int4_grouped.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p, _p]
+        L.quantize_int4_grouped.restype = _int
+        L.w4a16_linear.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p]
+        L.w4a16_linear.restype = _int
+        L.w4a16_linear_select.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
+                                          _p, _int, _p]
+        L.w4a16_linear_select.restype = _int
+        L.w4_status_string.argtypes = [_int]
+        L.w4_status_string.restype = ctypes.c_char_p
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().w4_status_string(int(status)).decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check(t, name, dtype, shape, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_ptr(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def quantize_int4_grouped(W, G: int, codes=None, scales=None, zeros=None):
+    """Quantize a bf16 GPU weight W[N, K] (group size G along K).
+
+    Returns (codes uint8 [N, K/2], scales bf16 [N, K/G], zeros bf16 [N, K/G]);
+    outputs are allocated when not given. Enqueued on torch's current stream.
+    """
+    torch = _torch()
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [N, K]")
+    N, K = W.shape
+    _check(W, "W", torch.bfloat16, (N, K))
+    ng = K // G if G else 0
+    if codes is None:
+        codes = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    if scales is None:
+        scales = torch.empty((N, ng), dtype=torch.bfloat16, device=W.device)
+    if zeros is None:
+        zeros = torch.empty((N, ng), dtype=torch.bfloat16, device=W.device)
+    _check(codes, "codes", torch.uint8, (N, K // 2), W.device)
+    _check(scales, "scales", torch.bfloat16, (N, ng), W.device)
+    _check(zeros, "zeros", torch.bfloat16, (N, ng), W.device)
+    st = lib().quantize_int4_grouped(W.data_ptr(), N, K, G, codes.data_ptr(),
+                                     scales.data_ptr(), zeros.data_ptr(),
+                                     _stream_ptr(W.device))
+    if st != W4Status.OK:
+        raise W4Error(st, "quantize_int4_grouped")
+    return codes, scales, zeros
+
+
+def w4a16_linear(x, codes, scales, zeros, G: int, bias=None, out=None,
+                 path: W4Path = W4Path.AUTO):
+    """y = x . dequant(codes, scales, zeros)^T (+ bias) for bf16 GPU x[M, K].
+
+    Returns y bf16 [M, N] (allocated when ``out`` is None). ``path`` forces
+    the GEMV or GEMM kernel (for tests); AUTO picks by M.
+    """
+    torch = _torch()
+    if x.dim() != 2 or codes.dim() != 2:
+        raise ValueError("x and codes must be 2-D")
+    M, K = x.shape
+    N = codes.shape[0]
+    ng = K // G if G else 0
+    _check(x, "x", torch.bfloat16, (M, K))
+    _check(codes, "codes", torch.uint8, (N, K // 2), x.device)
+    _check(scales, "scales", torch.bfloat16, (N, ng), x.device)
+    _check(zeros, "zeros", torch.bfloat16, (N, ng), x.device)
+    if bias is not None:
+        _check(bias, "bias", torch.bfloat16, (N,), x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(out, "out", torch.bfloat16, (M, N), x.device)
+    st = lib().w4a16_linear_select(
+        x.data_ptr(), M, codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+        bias.data_ptr() if bias is not None else None, N, K, G, out.data_ptr(),
+        int(path), _stream_ptr(x.device))
+    if st != W4Status.OK:
+        raise W4Error(st, "w4a16_linear")
+    return out

@@ -1,0 +1,118 @@
+// C interface of the W4A16 library: argument validation and kernel dispatch.
+// Every check runs before any HIP call; a failed check launches and writes
+// nothing. Declarations and the meaning of every argument: include/w4a16.h.
+#include "w4a16.h"
+#include "w4_launch.h"
+
+#include <stdint.h>
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;      // N and K
+constexpr int64_t kMaxM = int64_t(1) << 23;        // M (grid rows of the GEMM)
+constexpr int64_t kMaxElems = int64_t(1) << 40;    // N*K, M*K, M*N
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_group(int64_t G) { return G == 32 || G == 64 || G == 128; }
+
+// [p, p + bytes) overlaps [q, q + qbytes)?
+bool overlap(const void *p, int64_t bytes, const void *q, int64_t qbytes) {
+    if (!p || !q || bytes <= 0 || qbytes <= 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    const uintptr_t b = reinterpret_cast<uintptr_t>(q);
+    return a < b + static_cast<uintptr_t>(qbytes) && b < a + static_cast<uintptr_t>(bytes);
+}
+
+w4_status check_nkg(int64_t N, int64_t K, int64_t G) {
+    if (N < 1 || K < 1 || N > kMaxDim || K > kMaxDim) return W4_ERR_SHAPE;
+    if (!valid_group(G)) return W4_ERR_GROUP;
+    if (K % G != 0) return W4_ERR_SHAPE;
+    if (N * K > kMaxElems) return W4_ERR_SHAPE;
+    return W4_OK;
+}
+
+w4_status linear_impl(const uint16_t *x, int64_t M, const uint8_t *codes,
+                      const uint16_t *scales, const uint16_t *zeros,
+                      const uint16_t *bias, int64_t N, int64_t K, int64_t G,
+                      uint16_t *y, int path, hipStream_t stream) {
+    if (!codes || !scales || !zeros) return W4_ERR_NULL;
+    if (M > 0 && (!x || !y)) return W4_ERR_NULL;
+    if (M < 0 || M > kMaxM) return W4_ERR_SHAPE;
+    const w4_status st = check_nkg(N, K, G);
+    if (st != W4_OK) return st;
+    if (M * K > kMaxElems || M * N > kMaxElems) return W4_ERR_SHAPE;
+    if (path != W4_PATH_AUTO && path != W4_PATH_GEMV && path != W4_PATH_GEMM)
+        return W4_ERR_PATH;
+    if (path == W4_PATH_GEMV && M > W4_GEMV_MAX_M) return W4_ERR_PATH;
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(zeros) ||
+        (bias && !aligned16(bias)))
+        return W4_ERR_ALIGN;
+    if (M > 0 && (!aligned16(x) || !aligned16(y))) return W4_ERR_ALIGN;
+    if (M == 0) return W4_OK;
+    const int64_t ybytes = 2 * M * N;
+    if (overlap(y, ybytes, x, 2 * M * K) || overlap(y, ybytes, codes, N * K / 2) ||
+        overlap(y, ybytes, scales, 2 * N * (K / G)) ||
+        overlap(y, ybytes, zeros, 2 * N * (K / G)) || overlap(y, ybytes, bias, 2 * N))
+        return W4_ERR_ALIAS;
+
+    const bool gemv = path == W4_PATH_GEMV || (path == W4_PATH_AUTO && M <= W4_GEMV_MAX_M);
+    const hipError_t e =
+        gemv ? w4::launch_gemv(x, static_cast<int>(M), codes, scales, zeros, bias, N, K,
+                               static_cast<int>(G), y, stream)
+             : w4::launch_gemm(x, M, codes, scales, zeros, bias, N, K, static_cast<int>(G),
+                               y, stream);
+    return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
+} // namespace
+
+extern "C" {
+
+w4_status quantize_int4_grouped(const uint16_t *W, int64_t N, int64_t K, int64_t G,
+                                uint8_t *codes, uint16_t *scales, uint16_t *zeros,
+                                hipStream_t stream) {
+    if (!W || !codes || !scales || !zeros) return W4_ERR_NULL;
+    const w4_status st = check_nkg(N, K, G);
+    if (st != W4_OK) return st;
+    if (!aligned16(W) || !aligned16(codes) || !aligned16(scales) || !aligned16(zeros))
+        return W4_ERR_ALIGN;
+    const int64_t wbytes = 2 * N * K, cbytes = N * K / 2, sbytes = 2 * N * (K / G);
+    if (overlap(codes, cbytes, W, wbytes) || overlap(scales, sbytes, W, wbytes) ||
+        overlap(zeros, sbytes, W, wbytes) || overlap(codes, cbytes, scales, sbytes) ||
+        overlap(codes, cbytes, zeros, sbytes) || overlap(scales, sbytes, zeros, sbytes))
+        return W4_ERR_ALIAS;
+    const hipError_t e = w4::launch_quantize(W, N, K, static_cast<int>(G), codes, scales,
+                                             zeros, stream);
+    return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
+w4_status w4a16_linear(const uint16_t *x, int64_t M, const uint8_t *codes,
+                       const uint16_t *scales, const uint16_t *zeros,
+                       const uint16_t *bias, int64_t N, int64_t K, int64_t G,
+                       uint16_t *y, hipStream_t stream) {
+    return linear_impl(x, M, codes, scales, zeros, bias, N, K, G, y, W4_PATH_AUTO, stream);
+}
+
+w4_status w4a16_linear_select(const uint16_t *x, int64_t M, const uint8_t *codes,
+                              const uint16_t *scales, const uint16_t *zeros,
+                              const uint16_t *bias, int64_t N, int64_t K, int64_t G,
+                              uint16_t *y, int path, hipStream_t stream) {
+    return linear_impl(x, M, codes, scales, zeros, bias, N, K, G, y, path, stream);
+}
+
+const char *w4_status_string(int status) {
+    switch (status) {
+    case W4_OK: return "W4_OK: success";
+    case W4_ERR_NULL: return "W4_ERR_NULL: a required pointer is NULL";
+    case W4_ERR_SHAPE: return "W4_ERR_SHAPE: invalid or oversized N, K, M, or K % G != 0";
+    case W4_ERR_GROUP: return "W4_ERR_GROUP: group size must be 32, 64 or 128";
+    case W4_ERR_ALIGN: return "W4_ERR_ALIGN: pointers must be 16-byte aligned";
+    case W4_ERR_HIP: return "W4_ERR_HIP: the HIP runtime reported a launch error";
+    case W4_ERR_ALIAS: return "W4_ERR_ALIAS: an output overlaps an input";
+    case W4_ERR_PATH: return "W4_ERR_PATH: the requested kernel path cannot serve this call";
+    default: return "unknown w4_status";
+    }
+}
+
+} // extern "C"

@@ -1,0 +1,199 @@
+// Prefill-path W4A16 GEMM (any M, meant for M > 16) for gfx950.
+//
+// Same result as the GEMV: per output, in float32,
+//   sum_g ( s[n][g] * sum_{k in g} x[m][k] q[n][k] + z[n][g] * sum_{k in g} x[m][k] )
+// ("Optimum Quanto": wide accumulation, then dequantization; bias in float).
+//
+// Block tile 128 (m) x 128 (n), four waves in a 2 x 2 grid, 64 x 64 each.
+// K advances in stages of 64 (two 32-wide slices), double buffered in LDS:
+// the x tile is kept as bf16 (rows padded by 16 bytes against bank
+// conflicts) and the code tile as packed nibbles. For each slice a wave
+// expands its codes to the exact bf16 integers 128 + q and runs 16x16x32
+// bf16 MFMAs into a per-group accumulator; an MFMA against an all-ones B
+// gives the group sums of x in the same layout. At the end of a group:
+//   acc += s * acc_g + (z - 128 s) * xsum_g        (float32)
+#include "w4_device.h"
+#include "w4_launch.h"
+
+namespace w4 {
+
+namespace {
+
+constexpr int BM = 128, BN = 128, KS = 64;
+constexpr int A_LD = KS + 8;                   // bf16 elements per LDS row
+constexpr int B_LD = KS / 2 + 16;              // bytes per LDS code row
+constexpr int THREADS = 256;
+
+template <int G>
+__global__ __launch_bounds__(THREADS) void gemm_kernel(
+    const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y) {
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][A_LD];
+    __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN][B_LD];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int nl = lane & 15, kb = lane >> 4;
+    const int m0 = blockIdx.y * BM;
+    const int n0 = blockIdx.x * BN;
+    const int ngroups = K / G;
+    const int nstages = (K + KS - 1) / KS;
+    const int64_t code_ld = K >> 1;
+
+    // global -> LDS staging assignment
+    // x: 128 rows x 8 chunks of 16 B; thread handles chunks tid + 256 i
+    // codes: 128 rows x 2 chunks of 16 B; thread handles chunk tid
+    const int b_row = tid >> 1, b_half = tid & 1;
+    const int b_n = n0 + b_row;
+    const uint8_t *b_src = codes + static_cast<int64_t>(b_n < N ? b_n : N - 1) * code_ld;
+
+    auto load_stage = [&](int kt, u32x4 (&ra)[4], u32x4 &rb) {
+        const int k0 = kt * KS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + THREADS * i;
+            const int row = idx >> 3, col = (idx & 7) * 8;
+            const int m = m0 + row, k = k0 + col;
+            ra[i] = u32x4{0u, 0u, 0u, 0u};
+            if (m < M && k < K)
+                ra[i] = *reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(m) * K + k);
+        }
+        const int kc = k0 + b_half * 32;
+        rb = u32x4{0u, 0u, 0u, 0u};
+        if (b_n < N && kc < K)
+            rb = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(b_src + (kc >> 1)));
+    };
+    auto store_stage = [&](int buf, const u32x4 (&ra)[4], const u32x4 &rb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + THREADS * i;
+            const int row = idx >> 3, col = (idx & 7) * 8;
+            *reinterpret_cast<u32x4 *>(&As[buf][row][col]) = ra[i];
+        }
+        *reinterpret_cast<u32x4 *>(&Bs[buf][b_row][b_half * 16]) = rb;
+    };
+
+    f32x4 acc[4][4], accg[4][4], xsg[4];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = zero4;
+    const bf16x8 ones = bf16x8_ones();
+
+    int nrow[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int n = n0 + wn * 64 + nt * 16 + nl;
+        nrow[nt] = n < N ? n : N - 1;
+    }
+
+    {
+        u32x4 ra[4], rb;
+        load_stage(0, ra, rb);
+        store_stage(0, ra, rb);
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt < nstages; ++kt) {
+        const int cur = kt & 1;
+        u32x4 ra[4], rb;
+        const bool more = kt + 1 < nstages;
+        if (more) load_stage(kt + 1, ra, rb);
+
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+            const int k0 = kt * KS + sl * 32;
+            if (k0 >= K) break;
+            const bool first = (k0 % G) == 0;
+            const bool last = ((k0 + 32) % G) == 0;
+            float sv[4], zv[4];
+            if (last) {
+                const int g = (k0 + 32) / G - 1;
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    const int64_t si = static_cast<int64_t>(nrow[nt]) * ngroups + g;
+                    sv[nt] = bf16_to_f32(scales[si]);
+                    zv[nt] = bf16_to_f32(zeros[si]);
+                }
+            }
+            bf16x8 a[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                a[mt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+                    &As[cur][wm * 64 + mt * 16 + nl][sl * 32 + kb * 8]));
+            bf16x8 b[4];
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const uint32_t w = *reinterpret_cast<const uint32_t *>(
+                    &Bs[cur][wn * 64 + nt * 16 + nl][sl * 16 + kb * 4]);
+                uint32_t u[4];
+                unpack8_bias128(w, u);
+                b[nt] = as_bf16x8(u[0], u[1], u[2], u[3]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                xsg[mt] = mfma16x16x32(a[mt], ones, first ? zero4 : xsg[mt]);
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt)
+                    accg[mt][nt] = mfma16x16x32(a[mt], b[nt], first ? zero4 : accg[mt][nt]);
+            }
+            if (last) {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    const float zz = fmaf(-128.0f, sv[nt], zv[nt]);
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            acc[mt][nt][i] = fmaf(sv[nt], accg[mt][nt][i],
+                                                  fmaf(zz, xsg[mt][i], acc[mt][nt][i]));
+                }
+            }
+        }
+
+        if (more) store_stage(cur ^ 1, ra, rb);
+        __syncthreads();
+    }
+
+    // Store: lane holds rows 4*kb + i of each 16 x 16 tile, column nl.
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+        const int n = n0 + wn * 64 + nt * 16 + nl;
+        if (n >= N) continue;
+        const float bv = bias ? bf16_to_f32(bias[n]) : 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = m0 + wm * 64 + mt * 16 + 4 * kb + i;
+                if (m < M)
+                    y[static_cast<int64_t>(m) * N + n] =
+                        static_cast<uint16_t>(f32_to_bf16_rne(acc[mt][nt][i] + bv));
+            }
+    }
+}
+
+} // namespace
+
+hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *codes,
+                       const uint16_t *scales, const uint16_t *zeros,
+                       const uint16_t *bias, int64_t N, int64_t K, int G,
+                       uint16_t *y, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>((N + BN - 1) / BN),
+                    static_cast<unsigned>((M + BM - 1) / BM));
+    const dim3 block(THREADS);
+    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    switch (G) {
+    case 32: gemm_kernel<32><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, bias, n, k, y); break;
+    case 64: gemm_kernel<64><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, bias, n, k, y); break;
+    case 128: gemm_kernel<128><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, bias, n, k, y); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+} // namespace w4

@@ -1,0 +1,103 @@
+// Device helpers shared by the gfx950 kernels of the W4A16 library.
+//
+// bf16 values travel as raw 16-bit patterns. Codes are 4-bit unsigned
+// integers, two per byte, low nibble = even k.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 bits
+
+__device__ __forceinline__ float bf16_lo(uint32_t pair) {   // element 0
+    return __uint_as_float(pair << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t pair) {   // element 1
+    return __uint_as_float(pair & 0xFFFF0000u);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// binary32 -> bf16, round to nearest, ties to even (finite inputs; a carry
+// into the exponent is the correct rounding up).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ------------------------------------------------------------- DPP reduce
+// Min/max across aligned lane groups of 4, 8 or 16 lanes with DPP moves
+// (quad permutes, then half-row and row mirrors; each step leaves every
+// lane of the group holding the partial result of its whole sub-group).
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(
+        0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int DPP_QUAD_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141; // lane i <- lane 7-i within 8
+constexpr int DPP_ROW_MIRROR = 0x140;      // lane i <- lane 15-i within 16
+
+template <int LANES>
+__device__ __forceinline__ void group_minmax(float &mn, float &mx) {
+    static_assert(LANES == 4 || LANES == 8 || LANES == 16, "group lanes");
+    mn = fminf(mn, dpp_f32<DPP_QUAD_XOR1>(mn));
+    mx = fmaxf(mx, dpp_f32<DPP_QUAD_XOR1>(mx));
+    mn = fminf(mn, dpp_f32<DPP_QUAD_XOR2>(mn));
+    mx = fmaxf(mx, dpp_f32<DPP_QUAD_XOR2>(mx));
+    if constexpr (LANES >= 8) {
+        mn = fminf(mn, dpp_f32<DPP_ROW_HALF_MIRROR>(mn));
+        mx = fmaxf(mx, dpp_f32<DPP_ROW_HALF_MIRROR>(mx));
+    }
+    if constexpr (LANES >= 16) {
+        mn = fminf(mn, dpp_f32<DPP_ROW_MIRROR>(mn));
+        mx = fmaxf(mx, dpp_f32<DPP_ROW_MIRROR>(mx));
+    }
+}
+
+// ----------------------------------------------------------- code unpack
+// One dword of 8 codes (k = 0..7, natural order) -> four bf16 pairs holding
+// the exact integers 128 + q: bf16 0x4300 is 128.0 and its 7 mantissa bits
+// count in units of 1, so 0x4300 | q == 128 + q for q in 0..15.
+// out[i] = (128 + q[2i]) | (128 + q[2i+1]) << 16.
+__device__ __forceinline__ void unpack8_bias128(uint32_t w, uint32_t out[4]) {
+    const uint32_t w4 = w >> 4;
+    // byte0 <- w.byte i (q[2i] in its low nibble), byte2 <- (w>>4).byte i
+    // (q[2i+1] in its low nibble), bytes 1 and 3 <- 0.
+    out[0] = (__builtin_amdgcn_perm(w4, w, 0x0C040C00u) & 0x000F000Fu) | 0x43004300u;
+    out[1] = (__builtin_amdgcn_perm(w4, w, 0x0C050C01u) & 0x000F000Fu) | 0x43004300u;
+    out[2] = (__builtin_amdgcn_perm(w4, w, 0x0C060C02u) & 0x000F000Fu) | 0x43004300u;
+    out[3] = (__builtin_amdgcn_perm(w4, w, 0x0C070C03u) & 0x000F000Fu) | 0x43004300u;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    u32x4 u = {a, b, c, d};
+    return __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) {
+    return __builtin_bit_cast(bf16x8, u);
+}
+
+// bf16 1.0 in every element.
+__device__ __forceinline__ bf16x8 bf16x8_ones() {
+    return as_bf16x8(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+}
+
+// D = A(16x32) * B(32x16) + C on the bf16 matrix cores.
+// Lane l supplies A[l%16][8*(l/16) .. +8) and B[8*(l/16) .. +8)[l%16];
+// it receives D[4*(l/16) + i][l%16] in element i.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+} // namespace w4

@@ -1,0 +1,26 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// Arguments are already validated by the C interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+hipError_t launch_quantize(const uint16_t *W, int64_t N, int64_t K, int G,
+                           uint8_t *codes, uint16_t *scales, uint16_t *zeros,
+                           hipStream_t stream);
+
+// Decode GEMV, 1 <= M <= 16.
+hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *codes,
+                       const uint16_t *scales, const uint16_t *zeros,
+                       const uint16_t *bias, int64_t N, int64_t K, int G,
+                       uint16_t *y, hipStream_t stream);
+
+// Prefill GEMM, any M >= 1.
+hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *codes,
+                       const uint16_t *scales, const uint16_t *zeros,
+                       const uint16_t *bias, int64_t N, int64_t K, int G,
+                       uint16_t *y, hipStream_t stream);
+
+} // namespace w4

@@ -1,0 +1,141 @@
+/*
+ * w4a16.h - group-wise asymmetric int4 weight-only quantization and the
+ * W4A16 linear layer, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources are web pages, cited by title and section):
+ *   - "Optimum Quanto", "Design overview / Tensors": below 8 bits a tensor is
+ *     projected group-wise and affinely, with an offset ("zero-point"), onto
+ *     the target integer range, and mapped by rounding (torch.round: half to
+ *     even).
+ *   - "Optimum Quanto", "Modules": weights are quantized per output channel
+ *     along their first dimension; the bias is not quantized.
+ *   - "Optimum Quanto", "Pitfalls when quantizing activations": matmul
+ *     results are accumulated much wider than the inputs (float32) and then
+ *     dequantized.
+ *   - torchao README ("PyTorch原生训练至推理模型优化"), quick start, and
+ *     "torchao模型量化完全指南" section 3.1: int4 weight-only quantization
+ *     configured by a group size (32 recommended; 32/64/128 in use) applied
+ *     in place to nn.Linear weights [out_features, in_features].
+ *
+ * Data formats (all row-major, bf16 carried as raw uint16_t bits):
+ *   W      bf16  [N, K]      weight, N = out_features, K = in_features
+ *   codes  uint8 [N, K/2]    4-bit codes q in 0..15, two per byte:
+ *                            codes[n][j] = q[n][2j] | q[n][2j+1] << 4
+ *   scales bf16  [N, K/G]    s = bf16_rne((max - min) / 15)   (binary32 ops)
+ *   zeros  bf16  [N, K/G]    z = group minimum (the offset), +0 for zeros
+ *   dequantized weight       w_hat[n][k] = q[n][k] * s[n][k/G] + z[n][k/G]
+ *   x      bf16  [M, K],  bias bf16 [N] (optional),  y bf16 [M, N]
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers owned by the caller; every base pointer
+ *     must be 16-byte aligned. Outputs must not overlap inputs.
+ *   - Arguments are validated before any HIP call. On a validation error
+ *     nothing is launched and nothing is written; the status says why.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream).
+ *     A launch failure returns W4_ERR_HIP; faults during execution surface
+ *     at the caller's next synchronisation, as for any HIP kernel.
+ *   - The library keeps no state between calls and allocates no memory;
+ *     calls are reentrant. No C++ exception crosses the interface.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4_OK = 0,
+    W4_ERR_NULL = 1,   /* a required pointer is NULL                         */
+    W4_ERR_SHAPE = 2,  /* N < 1, K < 1, M < 0, K % G != 0, or size overflow  */
+    W4_ERR_GROUP = 3,  /* G not in {32, 64, 128}                             */
+    W4_ERR_ALIGN = 4,  /* a pointer is not 16-byte aligned                   */
+    W4_ERR_HIP = 5,    /* the HIP runtime reported a launch error            */
+    W4_ERR_ALIAS = 6,  /* an output buffer overlaps an input buffer          */
+    W4_ERR_PATH = 7    /* a forced kernel path cannot serve this M           */
+} w4_status;
+
+/* Kernel selection for w4a16_linear_select. AUTO is what w4a16_linear does:
+ * the decode GEMV for M <= 16, the prefill GEMM for M > 16. */
+typedef enum {
+    W4_PATH_AUTO = 0,
+    W4_PATH_GEMV = 1,  /* valid for 1 <= M <= 16 */
+    W4_PATH_GEMM = 2   /* valid for any M >= 1   */
+} w4_path;
+
+/* Largest M the decode GEMV serves. */
+#define W4_GEMV_MAX_M 16
+
+/*
+ * quantize_int4_grouped - quantize a bf16 weight W[N, K] with group size G
+ * along K ("Optimum Quanto", "Design overview / Tensors"; torchao int4
+ * weight-only config with group_size).
+ *
+ * For every row n and group g (elements k in [gG, gG+G)), in IEEE binary32:
+ *   lo = min(W) + 0, hi = max(W) + 0          (signed zeros made +0)
+ *   s  = bf16_rne((hi - lo) / 15)              (correctly rounded divide)
+ *   z  = lo                                    (exact: lo is an input)
+ *   q  = s == 0 ? 0 : clamp(rint((w - lo) / s), 0, 15)   (ties to even)
+ * and writes codes/scales/zeros in the formats above. Results are bit-exact
+ * and deterministic for finite inputs whose group range hi - lo is finite;
+ * for other inputs the outputs are unspecified (no fault).
+ *
+ * W       in   bf16 [N, K], read only; the caller may free it once the
+ *              stream has passed this call (the "freeze" step).
+ * N, K    in   N >= 1, K >= 1, K % G == 0
+ * G       in   32, 64 or 128
+ * codes   out  uint8 [N, K/2]
+ * scales  out  bf16  [N, K/G]
+ * zeros   out  bf16  [N, K/G]
+ */
+w4_status quantize_int4_grouped(const uint16_t *W, int64_t N, int64_t K,
+                                int64_t G, uint8_t *codes, uint16_t *scales,
+                                uint16_t *zeros, hipStream_t stream);
+
+/*
+ * w4a16_linear - y = x . w_hat^T (+ bias), the bf16-int4 mixed-precision
+ * linear ("Optimum Quanto": accelerated bf16-int4 matmul; accumulation wider
+ * than the inputs, then dequantization; bias kept in float).
+ *
+ * Each output is accumulated in float32 as
+ *   sum_g ( s[n][g] * sum_{k in g} x[m][k] * q[n][k] + z[n][g] * sum_{k in g} x[m][k] )
+ * plus bias[n] (if bias != NULL), then rounded to bf16 (nearest, ties to
+ * even). w_hat is never rounded to bf16. The summation order is the
+ * kernel's own, so results agree with an exact evaluation to float32
+ * accumulation error, not bit for bit.
+ *
+ * x       in   bf16 [M, K]; may be NULL when M == 0
+ * M       in   M >= 0; M == 0 returns W4_OK and launches nothing
+ * codes, scales, zeros   in   as produced by quantize_int4_grouped
+ * bias    in   bf16 [N] or NULL
+ * N, K, G in   as for quantize_int4_grouped
+ * y       out  bf16 [M, N]; may be NULL when M == 0
+ */
+w4_status w4a16_linear(const uint16_t *x, int64_t M, const uint8_t *codes,
+                       const uint16_t *scales, const uint16_t *zeros,
+                       const uint16_t *bias, int64_t N, int64_t K, int64_t G,
+                       uint16_t *y, hipStream_t stream);
+
+/*
+ * w4a16_linear_select - w4a16_linear with an explicit kernel choice, so both
+ * kernels can be exercised at the same M. Same arguments and results as
+ * w4a16_linear; returns W4_ERR_PATH if path is W4_PATH_GEMV and M > 16, or
+ * if path is not a w4_path value.
+ */
+w4_status w4a16_linear_select(const uint16_t *x, int64_t M,
+                              const uint8_t *codes, const uint16_t *scales,
+                              const uint16_t *zeros, const uint16_t *bias,
+                              int64_t N, int64_t K, int64_t G, uint16_t *y,
+                              int path, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *w4_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,132 @@
+"""The C interface on the CPU: the library loads, exports every function the
+header declares, and rejects invalid arguments before any HIP call (so no
+kernel is launched and no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_gemm_quantize_amd as w4
+from bit_gemm_quantize_amd.build import LIB_PATH, ROOT
+
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB_PATH):
+        from bit_gemm_quantize_amd.build import build
+        build()
+    return w4.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \t\*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted([
+        "quantize_int4_grouped", "w4a16_linear", "w4a16_linear_select",
+        "w4_status_string"])
+
+
+def test_library_exports_every_declared_function(L):
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} not exported by {LIB_PATH}"
+
+
+def test_status_strings(L):
+    for st in w4.W4Status:
+        s = w4.status_string(st)
+        assert s.startswith("W4_" + st.name), s
+    assert "unknown" in w4.status_string(99)
+
+
+# Fake device addresses: never dereferenced, because every call below fails
+# validation before the library touches HIP.
+A = 0x7F0000000000
+B = A + (1 << 32)
+C = B + (1 << 32)
+D = C + (1 << 32)
+E = D + (1 << 32)
+
+
+def q(L, W=A, N=64, K=128, G=32, codes=B, s=C, z=D):
+    return L.quantize_int4_grouped(W, N, K, G, codes, s, z, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(W=None), w4.W4Status.ERR_NULL),
+    (dict(codes=None), w4.W4Status.ERR_NULL),
+    (dict(s=None), w4.W4Status.ERR_NULL),
+    (dict(z=None), w4.W4Status.ERR_NULL),
+    (dict(N=0), w4.W4Status.ERR_SHAPE),
+    (dict(K=0), w4.W4Status.ERR_SHAPE),
+    (dict(N=-3), w4.W4Status.ERR_SHAPE),
+    (dict(G=48), w4.W4Status.ERR_GROUP),
+    (dict(G=16), w4.W4Status.ERR_GROUP),
+    (dict(G=256), w4.W4Status.ERR_GROUP),
+    (dict(K=96, G=64), w4.W4Status.ERR_SHAPE),
+    (dict(N=1 << 31), w4.W4Status.ERR_SHAPE),
+    (dict(W=A + 2), w4.W4Status.ERR_ALIGN),
+    (dict(codes=B + 8), w4.W4Status.ERR_ALIGN),
+    (dict(s=C + 4), w4.W4Status.ERR_ALIGN),
+    (dict(z=D + 1), w4.W4Status.ERR_ALIGN),
+    (dict(codes=A + 64), w4.W4Status.ERR_ALIAS),            # codes inside W
+    (dict(s=B + 16), w4.W4Status.ERR_ALIAS),                # scales inside codes
+    (dict(z=C), w4.W4Status.ERR_ALIAS),                     # zeros == scales
+])
+def test_quantize_validation(L, kw, expect):
+    assert q(L, **kw) == expect
+
+
+def lin(L, x=A, M=4, codes=B, s=C, z=D, bias=None, N=64, K=128, G=32, y=E, path=0):
+    return L.w4a16_linear_select(x, M, codes, s, z, bias, N, K, G, y, path, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(codes=None), w4.W4Status.ERR_NULL),
+    (dict(s=None), w4.W4Status.ERR_NULL),
+    (dict(z=None), w4.W4Status.ERR_NULL),
+    (dict(x=None), w4.W4Status.ERR_NULL),
+    (dict(y=None), w4.W4Status.ERR_NULL),
+    (dict(M=-1), w4.W4Status.ERR_SHAPE),
+    (dict(M=1 << 24), w4.W4Status.ERR_SHAPE),
+    (dict(N=0), w4.W4Status.ERR_SHAPE),
+    (dict(K=48, G=32), w4.W4Status.ERR_SHAPE),
+    (dict(G=100), w4.W4Status.ERR_GROUP),
+    (dict(path=3), w4.W4Status.ERR_PATH),
+    (dict(path=-1), w4.W4Status.ERR_PATH),
+    (dict(path=1, M=17), w4.W4Status.ERR_PATH),
+    (dict(x=A + 8), w4.W4Status.ERR_ALIGN),
+    (dict(y=E + 2), w4.W4Status.ERR_ALIGN),
+    (dict(bias=E + (1 << 30) + 6), w4.W4Status.ERR_ALIGN),
+    (dict(y=A + 256), w4.W4Status.ERR_ALIAS),                # y inside x
+    (dict(y=B), w4.W4Status.ERR_ALIAS),                      # y == codes
+    (dict(bias=E + 16), w4.W4Status.ERR_ALIAS),              # bias inside y
+    # M == 0: nothing to do, x and y may be NULL; nothing is launched
+    (dict(M=0, x=None, y=None), w4.W4Status.OK),
+    (dict(M=0), w4.W4Status.OK),
+    (dict(M=0, x=None, y=None, codes=None), w4.W4Status.ERR_NULL),
+    (dict(M=0, G=33), w4.W4Status.ERR_GROUP),
+])
+def test_linear_validation(L, kw, expect):
+    assert lin(L, **kw) == expect
+
+
+def test_linear_plain_entry_point_validates(L):
+    assert L.w4a16_linear(A, 1, None, C, D, None, 64, 128, 32, E, None) == w4.W4Status.ERR_NULL
+    assert L.w4a16_linear(A, 0, B, C, D, None, 64, 128, 32, E, None) == w4.W4Status.OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    W = torch.zeros(16, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        w4.quantize_int4_grouped(W, 32)
+    with pytest.raises(TypeError):
+        w4.quantize_int4_grouped(W.float(), 32)

@@ -1,0 +1,141 @@
+"""W4A16 linear on the GPU against the oracle (small seeded shapes that span
+several tiles and ragged tails, both kernels, bias, edge cases)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import gpu_util as gu
+from tests import pins
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def w4():
+    return gu.lib_or_skip()
+
+
+def run_case(w4, M, N, K, G, bias, path, seed, wstd=0.02, outliers=False):
+    W = workloads.random_bf16((N, K), wstd, seed)
+    if outliers:
+        cols = workloads.outlier_columns(K, seed)
+        W = workloads.normal_bf16_rows(N, K, wstd, seed, outlier_cols=cols)
+    x = workloads.random_bf16((M, K), 1.0, seed + 1)
+    b = workloads.random_bf16((1, N), 1.0, seed + 2)[0] if bias else None
+    codes, s, z = oracle.quantize_ref(W, G)
+    gu.log(f"linear M={M} N={N} K={K} G={G} bias={bias} path={path.name} seed={seed}")
+    # the GPU quantizes for itself; its output is checked bit-exact first
+    Wd = gu.to_dev_bf16(W)
+    cd, sd, zd = w4.quantize_int4_grouped(Wd, G)
+    gu.assert_quant_equal((cd.cpu().numpy(), gu.to_host_bits(sd), gu.to_host_bits(zd)),
+                          (codes, s, z), "quantize")
+    y = gu.Guarded((M, N), torch.bfloat16)
+    w4.w4a16_linear(gu.to_dev_bf16(x), cd, sd, zd, G,
+                    bias=gu.to_dev_bf16(b) if bias else None, out=y.tensor, path=path)
+    torch.cuda.synchronize()
+    y.check_guards()
+    y_ref = oracle.linear_ref(x, codes, s, z, G, b)
+    bound = gu.abs_bound(x, codes, s, z, G)
+    return gu.check_linear(gu.to_host_bits(y.tensor), y_ref, bound,
+                           what=f"M={M} N={N} K={K} G={G}")
+
+
+def test_tiny_config_auto(w4):
+    # nn.Linear(512, 512), group size 32, one input row
+    W = workloads.weight_bits(1, "linear")
+    x = workloads.activation_bits(1, 1, 512)
+    codes, s, z = oracle.quantize_ref(W, 32)
+    cd, sd, zd = w4.quantize_int4_grouped(gu.to_dev_bf16(W), 32)
+    y = w4.w4a16_linear(gu.to_dev_bf16(x), cd, sd, zd, 32)
+    torch.cuda.synchronize()
+    y_ref = oracle.linear_ref(x, codes, s, z, 32)
+    gu.check_linear(gu.to_host_bits(y), y_ref, gu.abs_bound(x, codes, s, z, 32), what="tiny",
+                    strict=True)
+
+
+GEMV_SHAPES = [(16, 128), (33, 256), (100, 96), (48, 320), (200, 1024), (17, 4096 + 128)]
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 15, 16])
+@pytest.mark.parametrize("shape", GEMV_SHAPES)
+def test_gemv(w4, G, M, shape):
+    N, K = shape
+    if K % G:
+        pytest.skip("K not a multiple of G")
+    run_case(w4, M, N, K, G, bias=(M % 2 == 1), path=gu_path(w4, "GEMV"), seed=N + K + M)
+
+
+GEMM_SHAPES = [(16, 64), (130, 320), (257, 512), (64, 96)]
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("M", [1, 16, 17, 33, 127, 128, 129, 257])
+@pytest.mark.parametrize("shape", GEMM_SHAPES)
+def test_gemm(w4, G, M, shape):
+    N, K = shape
+    if K % G:
+        pytest.skip("K not a multiple of G")
+    run_case(w4, M, N, K, G, bias=(M % 2 == 0), path=gu_path(w4, "GEMM"), seed=3 * N + K + M)
+
+
+@pytest.mark.parametrize("M", [1, 16, 40, 300])
+@pytest.mark.parametrize("G", [32, 128])
+def test_auto_dispatch_outliers(w4, M, G):
+    run_case(w4, M, 96, 1024, G, bias=True, path=gu_path(w4, "AUTO"), seed=M * 7 + G,
+             outliers=True)
+
+
+def gu_path(w4, name):
+    return getattr(w4.W4Path, name)
+
+
+def test_zero_input_gives_bias_exactly(w4):
+    N, K, G = 40, 256, 64
+    W = workloads.random_bf16((N, K), 0.02, 1)
+    b = workloads.random_bf16((1, N), 1.0, 2)[0]
+    cd, sd, zd = w4.quantize_int4_grouped(gu.to_dev_bf16(W), G)
+    for M, path in ((3, w4.W4Path.GEMV), (20, w4.W4Path.GEMM)):
+        x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+        y = w4.w4a16_linear(x, cd, sd, zd, G, bias=gu.to_dev_bf16(b), path=path)
+        torch.cuda.synchronize()
+        assert np.array_equal(gu.to_host_bits(y), np.tile(b, (M, 1)))
+
+
+def test_constant_groups_are_exact(w4):
+    # scale 0 everywhere: w_hat == w, and small-integer data makes y exact
+    N, K, G = 24, 256, 32
+    rng = np.random.default_rng(3)
+    vals = rng.integers(-3, 4, (N, K // G, 1)).repeat(G, axis=2).reshape(N, K)
+    W = pins.bf16_from_float(vals.astype(np.float64))
+    x = pins.bf16_from_float(rng.integers(-2, 3, (5, K)).astype(np.float64))
+    cd, sd, zd = w4.quantize_int4_grouped(gu.to_dev_bf16(W), G)
+    assert np.all(gu.to_host_bits(sd) == 0)
+    for path in (w4.W4Path.GEMV, w4.W4Path.GEMM):
+        y = w4.w4a16_linear(gu.to_dev_bf16(x), cd, sd, zd, G, path=path)
+        torch.cuda.synchronize()
+        exact = pins.f32_from_bf16(x).astype(np.float64) @ vals.T.astype(np.float64)
+        # integer sums are exact in float32; the only rounding is the bf16 store
+        assert np.array_equal(gu.to_host_bits(y), pins.bf16_from_float(exact))
+
+
+def test_m_zero_is_a_no_op(w4):
+    N, K, G = 16, 128, 32
+    cd, sd, zd = w4.quantize_int4_grouped(
+        gu.to_dev_bf16(workloads.random_bf16((N, K), 0.02, 4)), G)
+    x = torch.empty((0, K), dtype=torch.bfloat16, device="cuda")
+    y = w4.w4a16_linear(x, cd, sd, zd, G)
+    assert y.shape == (0, N)
+
+
+def test_linear_deterministic(w4):
+    N, K, G = 300, 1024, 64
+    W = workloads.random_bf16((N, K), 0.02, 9)
+    cd, sd, zd = w4.quantize_int4_grouped(gu.to_dev_bf16(W), G)
+    for M in (4, 200):
+        x = gu.to_dev_bf16(workloads.random_bf16((M, K), 1.0, 10))
+        a = gu.to_host_bits(w4.w4a16_linear(x, cd, sd, zd, G))
+        b = gu.to_host_bits(w4.w4a16_linear(x, cd, sd, zd, G))
+        assert np.array_equal(a, b)
