@@ -41,26 +41,31 @@ def linear_bytes(M, N, K, G):
     return N * K // 2 + 4 * N * K // G + 2 * M * K + 2 * M * N
 
 
-class Timer:
-    """HIP events around each launch, on the stream the kernels run on."""
+def graph_of(torch, fns):
+    """Capture the launches made by fns (in order) into one HIP graph."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for fn in fns:
+            fn()
+    torch.cuda.synchronize()
+    return g
 
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = {}
 
-    def run(self, name, fn):
-        ev0 = self.torch.cuda.Event(enable_timing=True)
-        ev1 = self.torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        fn()
-        ev1.record()
-        self.pairs.setdefault(name, []).append((ev0, ev1))
-
-    def total_ms(self, name):
-        return sum(a.elapsed_time(b) for a, b in self.pairs.get(name, []))
-
-    def count(self, name):
-        return len(self.pairs.get(name, []))
+def time_graphs(torch, graphs, reps, warmup=2):
+    """Replay the graphs round-robin; HIP events around the timed replays on
+    the current stream. Returns milliseconds per replay."""
+    for i in range(warmup * len(graphs)):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 def make_layer(torch, N, K, seed, M, dev):
@@ -72,11 +77,10 @@ def make_layer(torch, N, K, seed, M, dev):
     return W, x
 
 
-def cpu_baseline(layers, G, budget_s=25.0):
-    """Time the CPU oracle (quantize + M = 1 linear) on the first half of the
-    output rows of each decode layer, on this host's cores."""
-    import numpy as np
-
+def cpu_baseline(layers, G, min_s=10.0, max_s=30.0):
+    """Time the CPU oracle (quantize + M = 1 linear) on the decode layer set,
+    on this host's cores: whole layers, cycling through the set until at
+    least min_s of work has been timed (stopping early past max_s)."""
     import oracle
     import workloads
 
@@ -86,21 +90,23 @@ def cpu_baseline(layers, G, budget_s=25.0):
                             if i.get("user_api") == "blas"] or [1])
     except Exception:                                   # pragma: no cover
         blas_threads = 1
+    inputs = {name: (workloads.weight_bits(2, name), workloads.activation_bits(2, 1, K))
+              for name, (N, K) in layers.items()}
     total_bytes = 0
     t_total = 0.0
     done = []
-    for name, (N, K) in layers.items():
-        rows = N // 2
-        W = workloads.weight_bits(2, name, rows=(0, rows))
-        x = workloads.activation_bits(2, 1, K)
-        t0 = time.perf_counter()
-        c, s, z = oracle.quantize_ref(W, G)
-        oracle.linear_ref(x, c, s, z, G)
-        dt = time.perf_counter() - t0
-        t_total += dt
-        total_bytes += quant_bytes(rows, K, G) + linear_bytes(1, rows, K, G)
-        done.append(f"{name}[:{rows}]")
-        if t_total > budget_s:
+    while t_total < min_s:
+        for name, (N, K) in layers.items():
+            W, x = inputs[name]
+            t0 = time.perf_counter()
+            c, s, z = oracle.quantize_ref(W, G)
+            oracle.linear_ref(x, c, s, z, G)
+            t_total += time.perf_counter() - t0
+            total_bytes += quant_bytes(N, K, G) + linear_bytes(1, N, K, G)
+            done.append(name)
+            if t_total > max_s:
+                break
+        if t_total > max_s:
             break
     return {
         "value": round(total_bytes / t_total / 1e9, 4),
@@ -108,9 +114,9 @@ def cpu_baseline(layers, G, budget_s=25.0):
         "cores": int(blas_threads),
         "kind": "oracle",
         "sample": ("numpy oracle, quantize (single thread) + float64 M=1 linear "
-                   f"(BLAS, {blas_threads} threads) on the first half of the output "
-                   f"rows of {', '.join(done)}; {total_bytes / 1e6:.1f} MB of "
-                   f"algorithmic bytes in {t_total:.2f} s"),
+                   f"(BLAS, {blas_threads} threads) over whole decode layers "
+                   f"({len(done)} layer passes: {', '.join(done)}); "
+                   f"{total_bytes / 1e6:.1f} MB of algorithmic bytes in {t_total:.2f} s"),
         "host_cpus": os.cpu_count(),
         "host_affinity": len(os.sched_getaffinity(0)),
     }
@@ -143,8 +149,8 @@ def main():
     G = 128
     layers = dict(workloads.LLAMA3_8B)
     names = list(layers)
-    timer = Timer(torch)
     out = {}
+    reps = max(args.steps, 1)
 
     # ---- inputs of the step: rotating copies of the decode layer set -----
     set_bytes = sum(quant_bytes(N, K, G) for N, K in layers.values())
@@ -163,53 +169,68 @@ def main():
         sets.append(entry)
     torch.cuda.synchronize()
 
-    def step(r, timed):
-        e = sets[r % n_sets]
-        for name in names:
-            W, x, codes, sc, ze, y = e[name]
-            fn = (lambda W=W, c=codes, s=sc, z=ze: w4.quantize_int4_grouped(W, G, c, s, z))
-            timer.run(f"quantize:{name}", fn) if timed else fn()
-        for name in names:
-            W, x, codes, sc, ze, y = e[name]
-            fn = (lambda x=x, c=codes, s=sc, z=ze, y=y: w4.w4a16_linear(x, c, s, z, G, out=y))
-            timer.run(f"gemv:{name}", fn) if timed else fn()
+    def q_fn(e, name):
+        W, x, codes, sc, ze, y = e[name]
+        return lambda: w4.quantize_int4_grouped(W, G, codes, sc, ze)
+
+    def l_fn(e, name):
+        W, x, codes, sc, ze, y = e[name]
+        return lambda: w4.w4a16_linear(x, codes, sc, ze, G, out=y)
 
     step_bytes = sum(quant_bytes(N, K, G) + linear_bytes(1, N, K, G)
                      for N, K in layers.values())
     ms_per_step = None
+    q_ms_launch = {}
     if args.only in ("all", "step", "quantize"):
-        log(f"step: warmup {args.warmup}, timed {args.steps}")
+        # one graph per rotating copy: quantize the four layers, then the
+        # four M = 1 linears on the fresh codes
+        for e in sets:                      # eager warm-up of every launch
+            for name in names:
+                q_fn(e, name)()
+                l_fn(e, name)()
+        step_graphs = [graph_of(torch, [q_fn(e, n) for n in names] +
+                                [l_fn(e, n) for n in names]) for e in sets]
+        log(f"step: warmup {args.warmup}, timed {args.steps} (graph replays)")
         for i in range(args.warmup):
-            step(i, False)
+            step_graphs[i % n_sets].replay()
         torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        e0.record()
         for i in range(args.steps):
-            step(i, True)
+            step_graphs[i % n_sets].replay()
+        e1.record()
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ms_per_step = (t1 - t0) * 1e3 / args.steps
-        log(f"step: {ms_per_step:.4f} ms")
+        wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        ms_per_step = e0.elapsed_time(e1) / args.steps
+        log(f"step: {ms_per_step:.4f} ms (events), {wall_ms:.4f} ms (host clock)")
+        del step_graphs
 
-        q_ms = sum(timer.total_ms(f"quantize:{n}") for n in names)
-        g_ms = sum(timer.total_ms(f"gemv:{n}") for n in names)
-        q_bytes = args.steps * sum(quant_bytes(N, K, G) for N, K in layers.values())
-        g_bytes = args.steps * sum(linear_bytes(1, N, K, G) for N, K in layers.values())
+        # the quantizer alone, per layer: one graph of n_sets launches
+        per = {}
+        tot_b = 0
+        tot_ms = 0.0
+        for name, (N, K) in layers.items():
+            g = graph_of(torch, [q_fn(e, name) for e in sets])
+            ms = time_graphs(torch, [g], max(2, reps // n_sets)) / n_sets
+            q_ms_launch[name] = ms
+            b = quant_bytes(N, K, G)
+            per[name] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1)}
+            tot_b += b
+            tot_ms += ms
+            del g
         out["quantize"] = {
             "kernel": "quantize_kernel<128>", "bound": "hbm",
-            "achieved_GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
-            "frac": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "avg_launch_us": round(q_ms * 1e3 / timer.count(f"quantize:{names[0]}") / len(names), 3),
-            "per_layer_us": {n: round(timer.total_ms(f"quantize:{n}") * 1e3 / args.steps, 3)
-                             for n in names},
+            "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
+            "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_set": tot_b, "set_us": round(tot_ms * 1e3, 3),
+            "per_layer": per,
         }
-        out["gemv_in_step"] = {
-            "achieved_GBps": round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
-            "note": "codes were just written by the quantizer and may be cache resident",
-        }
-        out["_step"] = dict(q_ms=q_ms, g_ms=g_ms, q_bytes=q_bytes, g_bytes=g_bytes)
 
     # ---- decode GEMV on its own over rotating quantized copies ----------
-    if args.only in ("all", "gemv"):
+    g_ms_launch = {}
+    if args.only in ("all", "step", "gemv"):
         gset_bytes = sum(linear_bytes(1, N, K, G) for N, K in layers.values())
         n_g = max(2, -(-ROTATE_BYTES // gset_bytes))
         log(f"gemv: {n_g} rotating quantized copies of {gset_bytes / 1e6:.1f} MB")
@@ -219,34 +240,39 @@ def main():
             entry = {}
             for name, (N, K) in layers.items():
                 W, x = src[name][0], src[name][1]
-                c, s, z = w4.quantize_int4_grouped(W, G)
-                entry[name] = (x, c, s, z, torch.empty((1, N), dtype=torch.bfloat16, device=dev))
+                c, s_, z = w4.quantize_int4_grouped(W, G)
+                entry[name] = (x, c, s_, z, torch.empty((1, N), dtype=torch.bfloat16, device=dev))
             gsets.append(entry)
         torch.cuda.synchronize()
-        gt = Timer(torch)
-        for i in range(args.warmup + args.steps):
-            e = gsets[i % n_g]
-            for name in names:
-                x, c, s, z, y = e[name]
-                fn = (lambda x=x, c=c, s=s, z=z, y=y: w4.w4a16_linear(x, c, s, z, G, out=y))
-                gt.run(name, fn) if i >= args.warmup else fn()
-        torch.cuda.synchronize()
+
+        def g_fn(e, name):
+            x, c, s_, z, y = e[name]
+            return lambda: w4.w4a16_linear(x, c, s_, z, G, out=y)
+
         per = {}
         tot_ms = 0.0
         tot_b = 0
         for name, (N, K) in layers.items():
-            ms = gt.total_ms(name)
-            b = args.steps * linear_bytes(1, N, K, G)
-            per[name] = {"us": round(ms * 1e3 / args.steps, 3),
-                         "GBps": round(b / (ms * 1e-3) / 1e9, 1)}
+            g = graph_of(torch, [g_fn(e, name) for e in gsets])
+            ms = time_graphs(torch, [g], max(2, reps // 2)) / n_g
+            g_ms_launch[name] = ms
+            b = linear_bytes(1, N, K, G)
+            per[name] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1)}
             tot_ms += ms
             tot_b += b
+            del g
+        # the four layers back to back, as a decode step runs them
+        g = graph_of(torch, [g_fn(e, n) for e in gsets for n in names])
+        set_ms = time_graphs(torch, [g], max(2, reps // 2)) / n_g
+        del g
         out["gemv_m1"] = {
-            "kernel": "gemv_kernel<128,1,4>", "bound": "hbm",
+            "kernel": "gemv_kernel<128,8>", "bound": "hbm",
             "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
             "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_set": tot_b,
             "per_layer": per,
-            "set_us": round(tot_ms * 1e3 / args.steps, 3),
+            "set_back_to_back_us": round(set_ms * 1e3, 3),
+            "set_back_to_back_GBps": round(tot_b / (set_ms * 1e-3) / 1e9, 1),
         }
         del gsets
 
@@ -255,56 +281,65 @@ def main():
         M = 2048
         glayers = dict(workloads.GEMMA3_12B)
         log("gemm: Gemma3-12B-shaped layers, M=2048")
-        pre = {}
-        for i, (name, (N, K)) in enumerate(glayers.items()):
-            W, x = make_layer(torch, N, K, 50 + i, M, dev)
-            c, s, z = w4.quantize_int4_grouped(W, G)
-            pre[name] = (x, c, s, z, torch.empty((M, N), dtype=torch.bfloat16, device=dev))
-            del W
-        torch.cuda.synchronize()
-        gt = Timer(torch)
-        steps = max(5, args.steps // 2)
-        for i in range(args.warmup + steps):
-            for name in glayers:
-                x, c, s, z, y = pre[name]
-                fn = (lambda x=x, c=c, s=s, z=z, y=y: w4.w4a16_linear(x, c, s, z, G, out=y))
-                gt.run(name, fn) if i >= args.warmup else fn()
-        torch.cuda.synchronize()
         per = {}
         tot_ms = 0.0
         tot_f = 0
-        for name, (N, K) in glayers.items():
-            ms = gt.total_ms(name)
-            f = steps * 2 * M * N * K
-            per[name] = {"us": round(ms * 1e3 / steps, 2),
-                         "TFLOPs": round(f / (ms * 1e-3) / 1e12, 1)}
+        for i, (name, (N, K)) in enumerate(glayers.items()):
+            W, x = make_layer(torch, N, K, 50 + i, M, dev)
+            c, s_, z = w4.quantize_int4_grouped(W, G)
+            del W
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            fn = (lambda x=x, c=c, s_=s_, z=z, y=y: w4.w4a16_linear(x, c, s_, z, G, out=y))
+            fn()
+            g = graph_of(torch, [fn])
+            ms = time_graphs(torch, [g], max(3, reps // 5))
+            f = 2 * M * N * K
+            per[name] = {"us": round(ms * 1e3, 2), "TFLOPs": round(f / (ms * 1e-3) / 1e12, 1)}
             tot_ms += ms
             tot_f += f
+            del g, x, c, s_, z, y
         out["gemm_m2048"] = {
             "kernel": "gemm_kernel<128>", "bound": "mfma",
             "achieved_TFLOPs": round(tot_f / (tot_ms * 1e-3) / 1e12, 1),
             "frac": round(tot_f / (tot_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops_per_set": tot_f,
             "per_layer": per,
-            "set_us": round(tot_ms * 1e3 / steps, 2),
+            "set_us": round(tot_ms * 1e3, 2),
         }
-        del pre
+
+    # ---- achievable-bandwidth reference: torch's own device copy ----------
+    if args.only == "all":
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        g = graph_of(torch, [lambda: b.copy_(a)])
+        ms = time_graphs(torch, [g], 20)
+        out["hbm_reference"] = {"what": "torch device copy of 1 GiB (read + write)",
+                                "GBps": round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1)}
+        del a, b, g
 
     # ---- report ------------------------------------------------------------
-    st = out.pop("_step", None)
     roofline = None
     value = None
-    if st is not None:
+    if ms_per_step is not None:
         value = step_bytes / (ms_per_step * 1e-3) / 1e9
         # dominant kernel of the step: the one with the larger share of time
-        if st["q_ms"] >= st["g_ms"]:
-            a = st["q_bytes"] / (st["q_ms"] * 1e-3) / 1e9
-            name = "quantize_kernel<128>"
+        q_ms = sum(q_ms_launch.values())
+        g_ms = sum(g_ms_launch.values()) if g_ms_launch else 0.0
+        if q_ms >= g_ms:
+            b = sum(quant_bytes(N, K, G) for N, K in layers.values())
+            a_gbs = b / (q_ms * 1e-3) / 1e9
+            kname = "quantize_kernel<128>"
+            nl = len(q_ms_launch)
         else:
-            a = st["g_bytes"] / (st["g_ms"] * 1e-3) / 1e9
-            name = "gemv_kernel<128,1,4>"
-        roofline = {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": name}
+            b = sum(linear_bytes(1, N, K, G) for N, K in layers.values())
+            a_gbs = b / (g_ms * 1e-3) / 1e9
+            kname = "gemv_kernel<128,8>"
+            nl = len(g_ms_launch)
+        roofline = {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(a_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": kname,
+                    "avg_launch_us": round((q_ms if q_ms >= g_ms else g_ms) * 1e3 / nl, 3),
+                    "bytes_per_launch_avg": b // nl}
 
     cpu = None
     if not args.no_cpu_baseline and args.only == "all":
@@ -328,7 +363,8 @@ def main():
             "workload": "llama3_8b_decode_layer_set_m1_g128",
             "layers": {k: list(v) for k, v in layers.items()},
             "M": 1, "G": G,
-            "step": "quantize each layer's bf16 weight, then y = x . w_hat^T (M=1)",
+            "step": "quantize each layer's bf16 weight, then y = x . w_hat^T (M=1); "
+                    "one HIP graph replay per step",
             "step_bytes": step_bytes,
             "rotating_copies": n_sets,
         },

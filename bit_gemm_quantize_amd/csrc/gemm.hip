@@ -25,12 +25,13 @@ constexpr int B_LD = KS / 2 + 16;              // bytes per LDS code row
 constexpr int THREADS = 256;
 
 template <int G>
-__global__ __launch_bounds__(THREADS) void gemm_kernel(
+__global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y) {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][A_LD];
     __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN][B_LD];
+    __shared__ uint32_t SZ[2][2][BN];          // (s | z << 16) per group end
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -43,28 +44,33 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(
     const int nstages = (K + KS - 1) / KS;
     const int64_t code_ld = K >> 1;
 
-    // global -> LDS staging assignment
-    // x: 128 rows x 8 chunks of 16 B; thread handles chunks tid + 256 i
-    // codes: 128 rows x 2 chunks of 16 B; thread handles chunk tid
+    // Global -> LDS staging. Loads are unconditional with clamped addresses:
+    // rows past M or N only feed outputs that are never stored, and a stage
+    // past K (K % 64 == 32) is never read.
+    // x: 128 rows x 8 pieces of 16 B; thread handles pieces tid + 256 i.
+    // codes: 128 rows x 2 pieces of 16 B; thread handles piece tid.
+    const uint16_t *a_src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = tid + THREADS * i;
+        const int row = idx >> 3, col = (idx & 7) * 8;
+        a_src[i] = x + static_cast<int64_t>(min(m0 + row, M - 1)) * K + col;
+    }
     const int b_row = tid >> 1, b_half = tid & 1;
-    const int b_n = n0 + b_row;
-    const uint8_t *b_src = codes + static_cast<int64_t>(b_n < N ? b_n : N - 1) * code_ld;
+    const uint8_t *b_src = codes + static_cast<int64_t>(min(n0 + b_row, N - 1)) * code_ld +
+                           b_half * 16;
 
     auto load_stage = [&](int kt, u32x4 (&ra)[4], u32x4 &rb) {
         const int k0 = kt * KS;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int idx = tid + THREADS * i;
-            const int row = idx >> 3, col = (idx & 7) * 8;
-            const int m = m0 + row, k = k0 + col;
-            ra[i] = u32x4{0u, 0u, 0u, 0u};
-            if (m < M && k < K)
-                ra[i] = *reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(m) * K + k);
+            const int col = ((tid + THREADS * i) & 7) * 8;
+            // k = min(k0 + col, K - 8): stays inside the row
+            ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + min(k0, K - 8 - col));
         }
-        const int kc = k0 + b_half * 32;
-        rb = u32x4{0u, 0u, 0u, 0u};
-        if (b_n < N && kc < K)
-            rb = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(b_src + (kc >> 1)));
+        // k = min(k0 + 32 * half, K - 32)
+        rb = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+            b_src + min(k0, K - 32 - b_half * 32) / 2));
     };
     auto store_stage = [&](int buf, const u32x4 (&ra)[4], const u32x4 &rb) {
 #pragma unroll
@@ -76,6 +82,20 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(
         *reinterpret_cast<u32x4 *>(&Bs[buf][b_row][b_half * 16]) = rb;
     };
 
+    // Scales and zero-points of the groups that end inside a stage go
+    // through LDS with the tiles: thread t fetches row t % 128 of the block
+    // for group end h = t / 128 (for G = 32 one at the end of each slice,
+    // for G = 64 / 128 at most one, at the end of slice 1). The index is
+    // clamped; entries of groups that do not end are never read.
+    const int sz_row = tid & (BN - 1), sz_h = tid >> 7;
+    const int64_t sz_base = static_cast<int64_t>(min(n0 + sz_row, N - 1)) * ngroups;
+    auto load_sz = [&](int kt) -> uint32_t {
+        const int k_end = kt * KS + (G == 32 ? (sz_h + 1) * 32 : KS);
+        // for G = 128 no group ends in even stages: k_end / G - 1 can be -1
+        const int64_t g = sz_base + max(0, min(k_end / G - 1, ngroups - 1));
+        return static_cast<uint32_t>(scales[g]) | (static_cast<uint32_t>(zeros[g]) << 16);
+    };
+
     f32x4 acc[4][4], accg[4][4], xsg[4];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -83,26 +103,23 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = zero4;
     const bf16x8 ones = bf16x8_ones();
-
-    int nrow[4];
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int n = n0 + wn * 64 + nt * 16 + nl;
-        nrow[nt] = n < N ? n : N - 1;
-    }
+    const Unpack128 uc = unpack128_consts();
 
     {
         u32x4 ra[4], rb;
         load_stage(0, ra, rb);
+        const uint32_t sz = load_sz(0);
         store_stage(0, ra, rb);
+        SZ[0][sz_h][sz_row] = sz;
     }
     __syncthreads();
 
     for (int kt = 0; kt < nstages; ++kt) {
         const int cur = kt & 1;
-        u32x4 ra[4], rb;
         const bool more = kt + 1 < nstages;
-        if (more) load_stage(kt + 1, ra, rb);
+        u32x4 ra[4], rb;
+        load_stage(more ? kt + 1 : kt, ra, rb);
+        const uint32_t sz_nxt = load_sz(more ? kt + 1 : kt);
 
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl) {
@@ -110,16 +127,6 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(
             if (k0 >= K) break;
             const bool first = (k0 % G) == 0;
             const bool last = ((k0 + 32) % G) == 0;
-            float sv[4], zv[4];
-            if (last) {
-                const int g = (k0 + 32) / G - 1;
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    const int64_t si = static_cast<int64_t>(nrow[nt]) * ngroups + g;
-                    sv[nt] = bf16_to_f32(scales[si]);
-                    zv[nt] = bf16_to_f32(zeros[si]);
-                }
-            }
             bf16x8 a[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(
                 const uint32_t w = *reinterpret_cast<const uint32_t *>(
                     &Bs[cur][wn * 64 + nt * 16 + nl][sl * 16 + kb * 4]);
                 uint32_t u[4];
-                unpack8_bias128(w, u);
+                unpack8_bias128(w, u, uc);
                 b[nt] = as_bf16x8(u[0], u[1], u[2], u[3]);
             }
 #pragma unroll
@@ -142,20 +149,26 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(
                     accg[mt][nt] = mfma16x16x32(a[mt], b[nt], first ? zero4 : accg[mt][nt]);
             }
             if (last) {
+                const int h = (G == 32) ? sl : 0;
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
-                    const float zz = fmaf(-128.0f, sv[nt], zv[nt]);
+                    const uint32_t szv = SZ[cur][h][wn * 64 + nt * 16 + nl];
+                    const float sv = bf16_lo(szv);
+                    const float zz = fmaf(-128.0f, sv, bf16_hi(szv));
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
-                            acc[mt][nt][i] = fmaf(sv[nt], accg[mt][nt][i],
+                            acc[mt][nt][i] = fmaf(sv, accg[mt][nt][i],
                                                   fmaf(zz, xsg[mt][i], acc[mt][nt][i]));
                 }
             }
         }
 
-        if (more) store_stage(cur ^ 1, ra, rb);
+        if (more) {
+            store_stage(cur ^ 1, ra, rb);
+            SZ[cur ^ 1][sz_h][sz_row] = sz_nxt;
+        }
         __syncthreads();
     }
 

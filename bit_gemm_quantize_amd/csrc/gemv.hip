@@ -6,12 +6,16 @@
 // dequantized afterwards; bias kept in float.)
 //
 // The kernel streams the packed codes once from HBM. Work split:
-//   * a block owns 16*T output features (rows of the code matrix) and all
-//     of K; its NW waves split K into contiguous runs of 128-wide chunks and
+//   * a block owns 16 output features (rows of the code matrix) and all of
+//     K; its 8 waves split K into contiguous runs of 128-wide chunks and
 //     combine their partial sums through LDS at the end;
+//   * x[0:M, :] is staged once per block in LDS (in phases of columns when
+//     M*K does not fit) and read from there as the MFMA A operand;
 //   * per chunk, lane l (feature l%16, quarter kb = l/16) loads 16 bytes =
-//     32 codes (k = 128c + 32kb ... +32) with one 128-bit load per tile, so a
-//     wave load covers 64 contiguous bytes of each of 16 rows;
+//     32 codes (k = 128c + 32kb ... +32) with one 128-bit load, so a wave
+//     load covers 64 contiguous bytes of each of 16 rows; the codes, scales
+//     and zero-points of the next batch of chunks are in flight while the
+//     current batch is computed;
 //   * codes are expanded in registers to the exact bf16 integers 128 + q and
 //     fed with bf16 x to the 16x16x32 matrix-core op; M <= 16 rows of x fill
 //     the A operand (rows >= M are zero);
@@ -64,122 +68,153 @@ __device__ __forceinline__ void align_groups(u32x4 &d) {
     }
 }
 
-template <int G, int T, int NW>
-__global__ __launch_bounds__(NW * 64) void gemv_kernel(
+constexpr int GV_WAVES = 8;              // waves per block (split of K)
+constexpr int GV_X_ELEMS = 32768;        // bf16 elements of x staged in LDS
+
+// Codes, scales and zero-points of U consecutive chunks of one lane.
+template <int G, int U>
+struct Batch {
+    u32x4 q[U];
+    uint16_t s[U][128 / G];
+    uint16_t z[U][128 / G];
+};
+
+template <int G, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void gemv_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y) {
-    constexpr int SLOTS_PER_GROUP = G / 32;    // 4, 2 or 1 slots per group
-    __shared__ float red[NW][T][16][16];
+    constexpr int SPG = G / 32;                 // slots per group: 4, 2 or 1
+    constexpr int GPC = 128 / G;                // groups per chunk: 1, 2 or 4
+    constexpr int U = G == 32 ? 2 : 4;          // chunks per batch
+    __shared__ __attribute__((aligned(16))) uint16_t xl[GV_X_ELEMS];
+    __shared__ float red[NW][16][17];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nl = lane & 15;
     const int kb = lane >> 4;
-    const int n_base = blockIdx.x * 16 * T;
+    const int n_base = blockIdx.x * 16;
     const int nchunk = (K + 127) >> 7;
     const int ngroups = K / G;
-    const int c_begin = wave * nchunk / NW;
-    const int c_end = (wave + 1) * nchunk / NW;
+    const int n = n_base + nl < N ? n_base + nl : N - 1;   // clamped; masked on store
+    const uint8_t *crow = codes + static_cast<int64_t>(n) * (K >> 1);
+    const uint16_t *srow = scales + static_cast<int64_t>(n) * ngroups;
+    const uint16_t *zrow = zeros + static_cast<int64_t>(n) * ngroups;
+    // A-operand row of this lane. Rows >= M of the MFMA only feed outputs
+    // that are never stored, so they repeat row M-1 instead of being zeroed.
+    const int mrow = nl < M ? nl : M - 1;
+    const Unpack128 uc = unpack128_consts();
 
-    const bool m_ok = nl < M;                  // A-operand row of this lane
-    const uint16_t *xrow = x + static_cast<int64_t>(m_ok ? nl : 0) * K;
+    // x is staged in LDS in phases of kp columns (all of K when it fits),
+    // zero-padded to a whole chunk: codes past K (clamped reads below) then
+    // meet x = 0 and contribute nothing.
+    const int kp = min(nchunk * 128, (GV_X_ELEMS / M) & ~127);
+    const int cpp = kp >> 7;                    // chunks per phase
 
-    const uint8_t *crow[T];
-    int nrow[T];
+    // Loads are unconditional (clamped addresses), so the compiler can count
+    // the loads in flight and wait only for the batch being computed.
+    auto load = [&](Batch<G, U> &b, int c, int c_last) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        int n = n_base + 16 * t + nl;
-        nrow[t] = n < N ? n : N - 1;           // clamp; results masked on store
-        crow[t] = codes + static_cast<int64_t>(nrow[t]) * (K >> 1);
-    }
-
-    f32x4 acc[T];
+        for (int u = 0; u < U; ++u) {
+            const int cc = min(c + u, c_last);
+            const int kq = min(cc * 128 + kb * 32, K - 32);
+            b.q[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(crow + (kq >> 1)));
 #pragma unroll
-    for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int h = 0; h < GPC; ++h) {
+                const int g = min(cc * GPC + h, ngroups - 1);
+                b.s[u][h] = srow[g];
+                b.z[u][h] = zrow[g];
+            }
+        }
+    };
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     const bf16x8 ones = bf16x8_ones();
 
-    constexpr int U = 4;                       // chunks in flight per wave
-    for (int c0 = c_begin; c0 < c_end; c0 += U) {
-        u32x4 q[U][T];
-        u32x4 a[U][4];
+    auto compute = [&](Batch<G, U> &b, int c, int c_end, int k_phase) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int c = c0 + u;
-            const int kq = c * 128 + kb * 32;
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                q[u][t] = u32x4{0u, 0u, 0u, 0u};
-                if (c < c_end && kq < K)
-                    q[u][t] = __builtin_nontemporal_load(
-                        reinterpret_cast<const u32x4 *>(crow[t] + (kq >> 1)));
-            }
+            const int cc = c + u;
+            if (cc >= c_end) break;             // uniform across the wave
+            align_groups<G>(b.q[u]);
+            f32x4 accg = zero4, xsg = zero4;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int ka = c * 128 + slot_koff<G>(j, kb);
-                a[u][j] = u32x4{0u, 0u, 0u, 0u};
-                if (c < c_end && m_ok && ka < K)
-                    a[u][j] = *reinterpret_cast<const u32x4 *>(xrow + ka);
+                const bool first = (j % SPG) == 0;
+                const int ka = cc * 128 + slot_koff<G>(j, kb) - k_phase;
+                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(&xl[mrow * kp + ka]));
+                uint32_t w[4];
+                unpack8_bias128(b.q[u][j], w, uc);
+                xsg = mfma16x16x32(a, ones, first ? zero4 : xsg);
+                accg = mfma16x16x32(a, as_bf16x8(w[0], w[1], w[2], w[3]),
+                                    first ? zero4 : accg);
+                if ((j % SPG) == SPG - 1) {
+                    const int h = j / SPG;
+                    const float sv = bf16_to_f32(b.s[u][h]);
+                    const float zv = bf16_to_f32(b.z[u][h]);
+                    const float zz = fmaf(-128.0f, sv, zv);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[i] = fmaf(sv, accg[i], fmaf(zz, xsg[i], acc[i]));
+                }
             }
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = c0 + u;
+    };
+
+    for (int k_phase = 0; k_phase < K; k_phase += kp) {
+        const int pc0 = k_phase >> 7;
+        const int pc1 = min(nchunk, pc0 + cpp);
+        const int c_begin = pc0 + wave * (pc1 - pc0) / NW;
+        const int c_end = pc0 + (wave + 1) * (pc1 - pc0) / NW;
+        const int c_last = max(c_begin, c_end - 1);
+
+        // issue this wave's first code loads before staging x
+        Batch<G, U> b0, b1;
+        load(b0, c_begin, c_last);
+
+        // stage x[0:M, k_phase : k_phase + kp) (zero beyond K)
+        if (k_phase > 0) __syncthreads();        // previous phase fully consumed
+        const int kw = min(kp, ((K - k_phase + 127) >> 7) << 7);
+        const int per_row = kw >> 3;            // 16-byte pieces per row
+        for (int e = threadIdx.x; e < M * per_row; e += NW * 64) {
+            const int m = e / per_row;
+            const int kk = (e - m * per_row) * 8;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (k_phase + kk < K)
+                v = *reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(m) * K + k_phase + kk);
+            *reinterpret_cast<u32x4 *>(&xl[m * kp + kk]) = v;
+        }
+        __syncthreads();
+
+        int c = c_begin;
+        while (c < c_end) {
+            if (c + U < c_end) load(b1, c + U, c_last);
+            compute(b0, c, c_end, k_phase);
+            c += U;
             if (c >= c_end) break;
-#pragma unroll
-            for (int t = 0; t < T; ++t) align_groups<G>(q[u][t]);
-            f32x4 accg[T];
-            f32x4 xsg = zero4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const bool first = (j % SLOTS_PER_GROUP) == 0;
-                const bf16x8 av = as_bf16x8(a[u][j]);
-                xsg = mfma16x16x32(av, ones, first ? zero4 : xsg);
-#pragma unroll
-                for (int t = 0; t < T; ++t) {
-                    uint32_t b[4];
-                    unpack8_bias128(q[u][t][j], b);
-                    accg[t] = mfma16x16x32(av, as_bf16x8(b[0], b[1], b[2], b[3]),
-                                           first ? zero4 : accg[t]);
-                }
-                if ((j % SLOTS_PER_GROUP) == SLOTS_PER_GROUP - 1) {
-                    const int g = (c * 128 + 32 * (j - (SLOTS_PER_GROUP - 1))) / G;
-                    if (g < ngroups) {
-#pragma unroll
-                        for (int t = 0; t < T; ++t) {
-                            const int64_t si = static_cast<int64_t>(nrow[t]) * ngroups + g;
-                            const float s = bf16_to_f32(scales[si]);
-                            const float z = bf16_to_f32(zeros[si]);
-                            const float zz = fmaf(-128.0f, s, z);
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                acc[t][i] = fmaf(s, accg[t][i], fmaf(zz, xsg[i], acc[t][i]));
-                        }
-                    }
-                }
-            }
+            if (c + U < c_end) load(b0, c + U, c_last);
+            compute(b1, c, c_end, k_phase);
+            c += U;
         }
     }
 
     // Combine the waves' partial sums; lane holds rows 4*kb + i, column nl.
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave][t][4 * kb + i][nl] = acc[t][i];
+    for (int i = 0; i < 4; ++i) red[wave][4 * kb + i][nl] = acc[i];
     __syncthreads();
-    for (int e = threadIdx.x; e < T * M * 16; e += NW * 64) {
-        const int t = e / (M * 16);
-        const int r = e - t * (M * 16);
-        const int m = r >> 4;
-        const int nn = r & 15;
+    for (int e = threadIdx.x; e < M * 16; e += NW * 64) {
+        const int m = e >> 4;
+        const int nn = e & 15;
         float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) sum += red[w][t][m][nn];
-        const int n = n_base + 16 * t + nn;
-        if (n < N) {
-            if (bias) sum += bf16_to_f32(bias[n]);
-            y[static_cast<int64_t>(m) * N + n] = static_cast<uint16_t>(f32_to_bf16_rne(sum));
+        for (int w = 0; w < NW; ++w) sum += red[w][m][nn];
+        const int col = n_base + nn;
+        if (col < N) {
+            if (bias) sum += bf16_to_f32(bias[col]);
+            y[static_cast<int64_t>(m) * N + col] = static_cast<uint16_t>(f32_to_bf16_rne(sum));
         }
     }
 }
@@ -189,10 +224,9 @@ hipError_t launch_gemv_g(const uint16_t *x, int M, const uint8_t *codes,
                          const uint16_t *scales, const uint16_t *zeros,
                          const uint16_t *bias, int N, int K, uint16_t *y,
                          hipStream_t stream) {
-    constexpr int T = 1, NW = 4;
-    const dim3 grid((N + 16 * T - 1) / (16 * T)), block(NW * 64);
-    gemv_kernel<G, T, NW><<<grid, block, 0, stream>>>(x, M, codes, scales, zeros,
-                                                      bias, N, K, y);
+    const dim3 grid((N + 15) / 16), block(GV_WAVES * 64);
+    gemv_kernel<G, GV_WAVES><<<grid, block, 0, stream>>>(x, M, codes, scales, zeros,
+                                                         bias, N, K, y);
     return hipGetLastError();
 }
 

@@ -12,6 +12,7 @@ namespace w4 {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- bf16 bits
 
@@ -66,18 +67,40 @@ __device__ __forceinline__ void group_minmax(float &mn, float &mx) {
 }
 
 // ----------------------------------------------------------- code unpack
+// (a & mask) | c in one VALU op. gfx9 VOP3 takes no literal operands and at
+// most one scalar operand, so the mask comes in an SGPR and c in a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c) {
+    uint32_t d;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(c));
+    return d;
+}
+
+// Constants of the nibble expansion, materialised once per kernel.
+struct Unpack128 {
+    uint32_t mask;     // 0x000F000F (scalar)
+    uint32_t bias;     // 0x43004300 (vector)
+};
+__device__ __forceinline__ Unpack128 unpack128_consts() {
+    Unpack128 u;
+    u.mask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+    u.bias = 0x43004300u;
+    asm volatile("" : "+v"(u.bias));   // keep it in a VGPR
+    return u;
+}
+
 // One dword of 8 codes (k = 0..7, natural order) -> four bf16 pairs holding
 // the exact integers 128 + q: bf16 0x4300 is 128.0 and its 7 mantissa bits
 // count in units of 1, so 0x4300 | q == 128 + q for q in 0..15.
 // out[i] = (128 + q[2i]) | (128 + q[2i+1]) << 16.
-__device__ __forceinline__ void unpack8_bias128(uint32_t w, uint32_t out[4]) {
+__device__ __forceinline__ void unpack8_bias128(uint32_t w, uint32_t out[4],
+                                                const Unpack128 &c) {
     const uint32_t w4 = w >> 4;
     // byte0 <- w.byte i (q[2i] in its low nibble), byte2 <- (w>>4).byte i
     // (q[2i+1] in its low nibble), bytes 1 and 3 <- 0.
-    out[0] = (__builtin_amdgcn_perm(w4, w, 0x0C040C00u) & 0x000F000Fu) | 0x43004300u;
-    out[1] = (__builtin_amdgcn_perm(w4, w, 0x0C050C01u) & 0x000F000Fu) | 0x43004300u;
-    out[2] = (__builtin_amdgcn_perm(w4, w, 0x0C060C02u) & 0x000F000Fu) | 0x43004300u;
-    out[3] = (__builtin_amdgcn_perm(w4, w, 0x0C070C03u) & 0x000F000Fu) | 0x43004300u;
+    out[0] = and_or(__builtin_amdgcn_perm(w4, w, 0x0C040C00u), c.mask, c.bias);
+    out[1] = and_or(__builtin_amdgcn_perm(w4, w, 0x0C050C01u), c.mask, c.bias);
+    out[2] = and_or(__builtin_amdgcn_perm(w4, w, 0x0C060C02u), c.mask, c.bias);
+    out[3] = and_or(__builtin_amdgcn_perm(w4, w, 0x0C070C03u), c.mask, c.bias);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
