@@ -70,17 +70,57 @@ __device__ __forceinline__ void align_groups(u32x4 &d) {
 
 constexpr int GV_WAVES = 8;              // waves per block (split of K)
 constexpr int GV_X_ELEMS = 32768;        // bf16 elements of x staged in LDS
+constexpr int GV_STREAM_MAX_M = 4;      // persistent kernel: M <= 4
+constexpr int GV_STREAM_BLOCKS = 512;   // persistent kernel: 2 per compute unit
 
-// Codes, scales and zero-points of U consecutive chunks of one lane.
+// Codes of U consecutive chunks of one lane, plus the scales and zero-points
+// of the batch's U * 128 / G groups for the wave's 16 rows, loaded with
+// consecutive lanes on consecutive groups of a row: register r, lane l holds
+// (s | z << 16) of row l / 4, group 4r + l % 4 of the batch.
 template <int G, int U>
 struct Batch {
+    static constexpr int GPB = U * 128 / G;     // groups per batch (4 or 8)
+    static constexpr int R = GPB / 4;
     u32x4 q[U];
-    uint16_t s[U][128 / G];
-    uint16_t z[U][128 / G];
+    uint32_t s[R];
+    uint32_t z[R];
 };
 
+// Issue the loads of one batch: scales/zeros first (needed at the first
+// group end), then the codes. All addresses are clamped, never predicated.
+template <int G, int U>
+__device__ __forceinline__ void load_batch(Batch<G, U> &b, const uint8_t *crow,
+                                           const uint16_t *__restrict__ scales,
+                                           const uint16_t *__restrict__ zeros,
+                                           int row0, int N, int K, int ngroups,
+                                           int c, int c_last, int lane) {
+    constexpr int GPC = 128 / G;
+    const int kb = lane >> 4;
+    const int srow = min(row0 + (lane >> 2), N - 1);
+#pragma unroll
+    for (int r = 0; r < Batch<G, U>::R; ++r) {
+        const int g = min(c * GPC + 4 * r + (lane & 3), ngroups - 1);
+        const int64_t i = static_cast<int64_t>(srow) * ngroups + g;
+        b.s[r] = scales[i];
+        b.z[r] = zeros[i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int cc = min(c + u, c_last);
+        const int kq = min(cc * 128 + kb * 32, K - 32);
+        b.q[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(crow + (kq >> 1)));
+    }
+}
+
+// (s | z << 16) of group h of the batch for this lane's row (lane & 15),
+// fetched from the lane that loaded it; packed[r] = s[r] | z[r] << 16.
+__device__ __forceinline__ uint32_t batch_sz(const uint32_t *packed, int h, int lane) {
+    const int src = ((lane & 15) * 4 + (h & 3)) * 4;     // byte address of the source lane
+    return __builtin_amdgcn_ds_bpermute(src, packed[h >> 2]);
+}
+
 template <int G, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void gemv_kernel(
+__global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y) {
@@ -99,8 +139,6 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_kernel(
     const int ngroups = K / G;
     const int n = n_base + nl < N ? n_base + nl : N - 1;   // clamped; masked on store
     const uint8_t *crow = codes + static_cast<int64_t>(n) * (K >> 1);
-    const uint16_t *srow = scales + static_cast<int64_t>(n) * ngroups;
-    const uint16_t *zrow = zeros + static_cast<int64_t>(n) * ngroups;
     // A-operand row of this lane. Rows >= M of the MFMA only feed outputs
     // that are never stored, so they repeat row M-1 instead of being zeroed.
     const int mrow = nl < M ? nl : M - 1;
@@ -115,19 +153,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_kernel(
     // Loads are unconditional (clamped addresses), so the compiler can count
     // the loads in flight and wait only for the batch being computed.
     auto load = [&](Batch<G, U> &b, int c, int c_last) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int cc = min(c + u, c_last);
-            const int kq = min(cc * 128 + kb * 32, K - 32);
-            b.q[u] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4 *>(crow + (kq >> 1)));
-#pragma unroll
-            for (int h = 0; h < GPC; ++h) {
-                const int g = min(cc * GPC + h, ngroups - 1);
-                b.s[u][h] = srow[g];
-                b.z[u][h] = zrow[g];
-            }
-        }
+        load_batch<G, U>(b, crow, scales, zeros, n_base, N, K, ngroups, c, c_last, lane);
     };
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -141,21 +167,23 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_kernel(
             if (cc >= c_end) break;             // uniform across the wave
             align_groups<G>(b.q[u]);
             f32x4 accg = zero4, xsg = zero4;
+            uint32_t packed[Batch<G, U>::R];
+#pragma unroll
+            for (int r = 0; r < Batch<G, U>::R; ++r) packed[r] = (b.s[r] & 0xFFFFu) | (b.z[r] << 16);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bool first = (j % SPG) == 0;
                 const int ka = cc * 128 + slot_koff<G>(j, kb) - k_phase;
                 const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(&xl[mrow * kp + ka]));
                 uint32_t w[4];
-                unpack8_bias128(b.q[u][j], w, uc);
+                unpack8_bias128_il(b.q[u][j], w, uc);
                 xsg = mfma16x16x32(a, ones, first ? zero4 : xsg);
                 accg = mfma16x16x32(a, as_bf16x8(w[0], w[1], w[2], w[3]),
                                     first ? zero4 : accg);
                 if ((j % SPG) == SPG - 1) {
-                    const int h = j / SPG;
-                    const float sv = bf16_to_f32(b.s[u][h]);
-                    const float zv = bf16_to_f32(b.z[u][h]);
-                    const float zz = fmaf(-128.0f, sv, zv);
+                    const uint32_t szv = batch_sz(packed, u * GPC + j / SPG, lane);
+                    const float sv = bf16_lo(szv);
+                    const float zz = fmaf(-128.0f, sv, bf16_hi(szv));
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         acc[i] = fmaf(sv, accg[i], fmaf(zz, xsg[i], acc[i]));
@@ -185,7 +213,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_kernel(
             u32x4 v = {0u, 0u, 0u, 0u};
             if (k_phase + kk < K)
                 v = *reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(m) * K + k_phase + kk);
-            *reinterpret_cast<u32x4 *>(&xl[m * kp + kk]) = v;
+            *reinterpret_cast<u32x4 *>(&xl[m * kp + kk]) = interleave8_bf16(v);
         }
         __syncthreads();
 
@@ -219,14 +247,155 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_kernel(
     }
 }
 
+// Persistent variant for M * K small enough to keep x in LDS for the whole
+// block: the block stages x once, then streams 16-row tiles blockIdx.x,
+// blockIdx.x + gridDim.x, ...; each wave keeps the same run of K chunks for
+// every tile, and the codes of the next (tile, batch) are in flight while
+// the current one is computed, so HBM stays busy across tiles. One barrier
+// per tile combines the waves' partial sums (double-buffered).
+template <int G, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void gemv_stream_kernel(
+    const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y) {
+    constexpr int SPG = G / 32;
+    constexpr int GPC = 128 / G;
+    constexpr int U = G == 32 ? 2 : 4;
+    __shared__ __attribute__((aligned(16))) uint16_t xl[GV_X_ELEMS];
+    __shared__ float red[2][NW][GV_STREAM_MAX_M][16];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nl = lane & 15;
+    const int kb = lane >> 4;
+    const int nchunk = (K + 127) >> 7;
+    const int kr = nchunk * 128;                // LDS row length (zero padded)
+    const int ngroups = K / G;
+    const int ntiles = (N + 15) >> 4;
+    const int my_tiles = (ntiles - static_cast<int>(blockIdx.x) + gridDim.x - 1) / gridDim.x;
+    const int mrow = nl < M ? nl : M - 1;
+    const Unpack128 uc = unpack128_consts();
+
+    // this wave's run of chunks, the same for every tile; nb batches per
+    // tile for every wave (short runs leave their last batch partly idle)
+    const int cb = wave * nchunk / NW;
+    const int ce = (wave + 1) * nchunk / NW;
+    const int c_last = max(cb, ce - 1);
+    const int nb = ((nchunk + NW - 1) / NW + U - 1) / U;
+    const int nitems = my_tiles * nb;
+
+    auto load = [&](Batch<G, U> &b, int item) {
+        const int t = item / nb;
+        const int c = cb + (item - t * nb) * U;
+        const int tile = blockIdx.x + t * gridDim.x;
+        const int n = min(tile * 16 + nl, N - 1);
+        load_batch<G, U>(b, codes + static_cast<int64_t>(n) * (K >> 1), scales, zeros,
+                         tile * 16, N, K, ngroups, c, c_last, lane);
+    };
+
+    // issue the first loads, then stage all of x (interleaved, zero padded)
+    Batch<G, U> b0, b1;
+    if (nitems > 0) load(b0, 0);
+    const int per_row = kr >> 3;
+    for (int e = threadIdx.x; e < M * per_row; e += NW * 64) {
+        const int m = e / per_row;
+        const int kk = (e - m * per_row) * 8;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (kk < K)
+            v = *reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(m) * K + kk);
+        *reinterpret_cast<u32x4 *>(&xl[m * kr + kk]) = interleave8_bf16(v);
+    }
+    __syncthreads();
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    const bf16x8 ones = bf16x8_ones();
+
+    auto step = [&](Batch<G, U> &b, int item) {
+        const int t = item / nb;
+        const int bi = item - t * nb;
+        const int c = cb + bi * U;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int cc = c + u;
+            if (cc >= ce) break;                // uniform across the wave
+            align_groups<G>(b.q[u]);
+            f32x4 accg = zero4, xsg = zero4;
+            uint32_t packed[Batch<G, U>::R];
+#pragma unroll
+            for (int r = 0; r < Batch<G, U>::R; ++r) packed[r] = (b.s[r] & 0xFFFFu) | (b.z[r] << 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool first = (j % SPG) == 0;
+                const int ka = cc * 128 + slot_koff<G>(j, kb);
+                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(&xl[mrow * kr + ka]));
+                uint32_t w[4];
+                unpack8_bias128_il(b.q[u][j], w, uc);
+                xsg = mfma16x16x32(a, ones, first ? zero4 : xsg);
+                accg = mfma16x16x32(a, as_bf16x8(w[0], w[1], w[2], w[3]),
+                                    first ? zero4 : accg);
+                if ((j % SPG) == SPG - 1) {
+                    const uint32_t szv = batch_sz(packed, u * GPC + j / SPG, lane);
+                    const float sv = bf16_lo(szv);
+                    const float zz = fmaf(-128.0f, sv, bf16_hi(szv));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[i] = fmaf(sv, accg[i], fmaf(zz, xsg[i], acc[i]));
+                }
+            }
+        }
+        if (bi == nb - 1) {                     // end of tile t: combine waves
+            const int par = t & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * kb + i < M) red[par][wave][4 * kb + i][nl] = acc[i];
+            acc = zero4;
+            __syncthreads();
+            const int tile = blockIdx.x + t * gridDim.x;
+            for (int e = threadIdx.x; e < M * 16; e += NW * 64) {
+                const int m = e >> 4;
+                const int nn = e & 15;
+                float sum = 0.f;
+#pragma unroll
+                for (int w = 0; w < NW; ++w) sum += red[par][w][m][nn];
+                const int col = tile * 16 + nn;
+                if (col < N) {
+                    if (bias) sum += bf16_to_f32(bias[col]);
+                    y[static_cast<int64_t>(m) * N + col] =
+                        static_cast<uint16_t>(f32_to_bf16_rne(sum));
+                }
+            }
+        }
+    };
+
+    int i = 0;
+    while (i < nitems) {
+        if (i + 1 < nitems) load(b1, i + 1);
+        step(b0, i);
+        if (++i >= nitems) break;
+        if (i + 1 < nitems) load(b0, i + 1);
+        step(b1, i);
+        ++i;
+    }
+}
+
 template <int G>
 hipError_t launch_gemv_g(const uint16_t *x, int M, const uint8_t *codes,
                          const uint16_t *scales, const uint16_t *zeros,
                          const uint16_t *bias, int N, int K, uint16_t *y,
                          hipStream_t stream) {
-    const dim3 grid((N + 15) / 16), block(GV_WAVES * 64);
-    gemv_kernel<G, GV_WAVES><<<grid, block, 0, stream>>>(x, M, codes, scales, zeros,
-                                                         bias, N, K, y);
+    const int ntiles = (N + 15) / 16;
+    const int kr = (K + 127) / 128 * 128;
+    const dim3 block(GV_WAVES * 64);
+    if (M <= GV_STREAM_MAX_M && static_cast<int64_t>(M) * kr <= GV_X_ELEMS) {
+        // two resident blocks per compute unit, each streaming several tiles
+        const int blocks = ntiles < GV_STREAM_BLOCKS ? ntiles : GV_STREAM_BLOCKS;
+        gemv_stream_kernel<G, GV_WAVES><<<dim3(blocks), block, 0, stream>>>(
+            x, M, codes, scales, zeros, bias, N, K, y);
+    } else {
+        gemv_phased_kernel<G, GV_WAVES><<<dim3(ntiles), block, 0, stream>>>(
+            x, M, codes, scales, zeros, bias, N, K, y);
+    }
     return hipGetLastError();
 }
 

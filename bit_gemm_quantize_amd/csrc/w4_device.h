@@ -103,6 +103,29 @@ __device__ __forceinline__ void unpack8_bias128(uint32_t w, uint32_t out[4],
     out[3] = and_or(__builtin_amdgcn_perm(w4, w, 0x0C070C03u), c.mask, c.bias);
 }
 
+// One dword of 8 codes -> four bf16 pairs of 128 + q in the interleaved
+// order (q0,q4), (q1,q5), (q2,q6), (q3,q7): k = 0,4,1,5,2,6,3,7. The other
+// MFMA operand must list its 8 values in the same order (see
+// interleave8_bf16). 7 VALU ops instead of 9.
+__device__ __forceinline__ void unpack8_bias128_il(uint32_t w, uint32_t out[4],
+                                                   const Unpack128 &c) {
+    out[0] = and_or(w, c.mask, c.bias);
+    out[1] = and_or(w >> 4, c.mask, c.bias);
+    out[2] = and_or(w >> 8, c.mask, c.bias);
+    out[3] = and_or(w >> 12, c.mask, c.bias);
+}
+
+// 8 consecutive bf16 (k = 0..7, as 4 dwords of pairs) -> the interleaved
+// order k = 0,4,1,5,2,6,3,7 used by unpack8_bias128_il.
+__device__ __forceinline__ u32x4 interleave8_bf16(u32x4 v) {
+    u32x4 r;
+    r.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);   // (x0, x4)
+    r.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);   // (x1, x5)
+    r.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);   // (x2, x6)
+    r.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);   // (x3, x7)
+    return r;
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     u32x4 u = {a, b, c, d};
     return __builtin_bit_cast(bf16x8, u);
