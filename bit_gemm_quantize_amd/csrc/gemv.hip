@@ -71,7 +71,9 @@ __device__ __forceinline__ void align_groups(u32x4 &d) {
 constexpr int GV_WAVES = 8;              // waves per block (split of K)
 constexpr int GV_X_ELEMS = 32768;        // bf16 elements of x staged in LDS
 constexpr int GV_STREAM_MAX_M = 4;      // persistent kernel: M <= 4
-constexpr int GV_STREAM_BLOCKS = 512;   // persistent kernel: 2 per compute unit
+constexpr int GV_STREAM_WAVES = 8;      // persistent kernel: waves per block
+constexpr int GV_STREAM_MAX_LDS = GV_X_ELEMS * 2 + (GV_X_ELEMS / 32) * 4 * 4 +
+                                  2 * GV_STREAM_WAVES * 4 * 16 * 4;
 
 // Codes of U consecutive chunks of one lane, plus the scales and zero-points
 // of the batch's U * 128 / G groups for the wave's 16 rows, loaded with
@@ -247,12 +249,14 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
     }
 }
 
-// Persistent variant for M * K small enough to keep x in LDS for the whole
-// block: the block stages x once, then streams 16-row tiles blockIdx.x,
-// blockIdx.x + gridDim.x, ...; each wave keeps the same run of K chunks for
-// every tile, and the codes of the next (tile, batch) are in flight while
-// the current one is computed, so HBM stays busy across tiles. One barrier
-// per tile combines the waves' partial sums (double-buffered).
+// Persistent variant for M <= 4 and M * K small enough to keep x in LDS:
+// one block per compute unit stages x once (interleaved, zero padded to
+// whole chunks) together with the per-group sums xs[g][m] = sum_{k in g}
+// x[m][k], then streams 16-row tiles blockIdx.x, blockIdx.x + gridDim.x, ...
+// Each wave keeps the same run of K chunks for every tile, and the codes of
+// the next (tile, batch) are in flight while the current one is computed.
+// One barrier per tile combines the waves' partial sums (double-buffered).
+// Only lanes 0..15 (rows 0..3 of the MFMA output) carry live outputs.
 template <int G, int NW>
 __global__ __launch_bounds__(NW * 64, 2) void gemv_stream_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
@@ -261,8 +265,9 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_stream_kernel(
     constexpr int SPG = G / 32;
     constexpr int GPC = 128 / G;
     constexpr int U = G == 32 ? 2 : 4;
-    __shared__ __attribute__((aligned(16))) uint16_t xl[GV_X_ELEMS];
-    __shared__ float red[2][NW][GV_STREAM_MAX_M][16];
+    constexpr int LPG = G / 8;                  // staging lanes per group
+    // dynamic LDS: x [M][kr] bf16 | xs [kr/G][4] f32 | red [2][NW][4][16] f32
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -270,14 +275,17 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_stream_kernel(
     const int kb = lane >> 4;
     const int nchunk = (K + 127) >> 7;
     const int kr = nchunk * 128;                // LDS row length (zero padded)
+    uint16_t *xl = reinterpret_cast<uint16_t *>(smem);
+    float(*xs)[GV_STREAM_MAX_M] = reinterpret_cast<float(*)[GV_STREAM_MAX_M]>(
+        smem + static_cast<size_t>(M) * kr * 2);
+    float(*red)[NW][GV_STREAM_MAX_M][16] = reinterpret_cast<float(*)[NW][GV_STREAM_MAX_M][16]>(
+        smem + static_cast<size_t>(M) * kr * 2 + static_cast<size_t>(kr / G) * GV_STREAM_MAX_M * 4);
     const int ngroups = K / G;
     const int ntiles = (N + 15) >> 4;
     const int my_tiles = (ntiles - static_cast<int>(blockIdx.x) + gridDim.x - 1) / gridDim.x;
     const int mrow = nl < M ? nl : M - 1;
     const Unpack128 uc = unpack128_consts();
 
-    // this wave's run of chunks, the same for every tile; nb batches per
-    // tile for every wave (short runs leave their last batch partly idle)
     const int cb = wave * nchunk / NW;
     const int ce = (wave + 1) * nchunk / NW;
     const int c_last = max(cb, ce - 1);
@@ -293,37 +301,42 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_stream_kernel(
                          tile * 16, N, K, ngroups, c, c_last, lane);
     };
 
-    // issue the first loads, then stage all of x (interleaved, zero padded)
+    // issue the first loads, then stage x and its group sums
     Batch<G, U> b0, b1;
     if (nitems > 0) load(b0, 0);
-    const int per_row = kr >> 3;
+    const int per_row = kr >> 3;                // 16-byte pieces per row
     for (int e = threadIdx.x; e < M * per_row; e += NW * 64) {
+        // a group's LPG pieces are consecutive lanes (M * per_row and the
+        // stride are multiples of LPG), so they reduce with DPP moves
         const int m = e / per_row;
         const int kk = (e - m * per_row) * 8;
         u32x4 v = {0u, 0u, 0u, 0u};
         if (kk < K)
             v = *reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(m) * K + kk);
         *reinterpret_cast<u32x4 *>(&xl[m * kr + kk]) = interleave8_bf16(v);
+        float sum = (bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y)) +
+                    (bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w));
+        sum = group_sum<LPG>(sum);
+        if (((e & (LPG - 1)) == 0)) xs[kk / G][m] = sum;
     }
     __syncthreads();
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-    const bf16x8 ones = bf16x8_ones();
 
     auto step = [&](Batch<G, U> &b, int item) {
         const int t = item / nb;
         const int bi = item - t * nb;
         const int c = cb + bi * U;
+        uint32_t packed[Batch<G, U>::R];
+#pragma unroll
+        for (int r = 0; r < Batch<G, U>::R; ++r) packed[r] = (b.s[r] & 0xFFFFu) | (b.z[r] << 16);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int cc = c + u;
             if (cc >= ce) break;                // uniform across the wave
             align_groups<G>(b.q[u]);
-            f32x4 accg = zero4, xsg = zero4;
-            uint32_t packed[Batch<G, U>::R];
-#pragma unroll
-            for (int r = 0; r < Batch<G, U>::R; ++r) packed[r] = (b.s[r] & 0xFFFFu) | (b.z[r] << 16);
+            f32x4 accg = zero4;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bool first = (j % SPG) == 0;
@@ -331,24 +344,31 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_stream_kernel(
                 const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(&xl[mrow * kr + ka]));
                 uint32_t w[4];
                 unpack8_bias128_il(b.q[u][j], w, uc);
-                xsg = mfma16x16x32(a, ones, first ? zero4 : xsg);
                 accg = mfma16x16x32(a, as_bf16x8(w[0], w[1], w[2], w[3]),
                                     first ? zero4 : accg);
                 if ((j % SPG) == SPG - 1) {
-                    const uint32_t szv = batch_sz(packed, u * GPC + j / SPG, lane);
+                    const int h = u * GPC + j / SPG;
+                    const uint32_t szv = batch_sz(packed, h, lane);
                     const float sv = bf16_lo(szv);
                     const float zz = fmaf(-128.0f, sv, bf16_hi(szv));
+                    const f32x4 xg = *reinterpret_cast<const f32x4 *>(&xs[cc * GPC + j / SPG][0]);
+                    // All four MFMA results are consumed (also for M = 1):
+                    // leaving some of them dead lets the register allocator
+                    // reuse an MFMA destination register while the MFMA is
+                    // still writing it, which gave wrong results.
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        acc[i] = fmaf(sv, accg[i], fmaf(zz, xsg[i], acc[i]));
+                        acc[i] = fmaf(sv, accg[i], fmaf(zz, xg[i], acc[i]));
                 }
             }
         }
         if (bi == nb - 1) {                     // end of tile t: combine waves
             const int par = t & 1;
+            if (kb == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (4 * kb + i < M) red[par][wave][4 * kb + i][nl] = acc[i];
+                for (int i = 0; i < GV_STREAM_MAX_M; ++i)
+                    if (i < M) red[par][wave][i][nl] = acc[i];
+            }
             acc = zero4;
             __syncthreads();
             const int tile = blockIdx.x + t * gridDim.x;
@@ -379,6 +399,51 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_stream_kernel(
     }
 }
 
+int compute_units() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+template <int G>
+hipError_t launch_stream(const uint16_t *x, int M, const uint8_t *codes,
+                         const uint16_t *scales, const uint16_t *zeros,
+                         const uint16_t *bias, int N, int K, uint16_t *y,
+                         hipStream_t stream) {
+    constexpr int NW = GV_STREAM_WAVES;
+    auto kern = gemv_stream_kernel<G, NW>;
+    static bool attr_set[64] = {false};         // per device
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 GV_STREAM_MAX_LDS);
+        if (e != hipSuccess) return e;
+        if (dev >= 0 && dev < 64) attr_set[dev] = true;
+    }
+    const int ntiles = (N + 15) / 16;
+    const int kr = (K + 127) / 128 * 128;
+    const size_t lds = static_cast<size_t>(M) * kr * 2 +
+                       static_cast<size_t>(kr / G) * GV_STREAM_MAX_M * 4 +
+                       2 * NW * GV_STREAM_MAX_M * 16 * 4;
+    // resident blocks per compute unit: LDS (160 KB) and 2 blocks of NW waves
+    int per_cu = static_cast<int>((160 * 1024) / lds);
+    per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
+    const int slots = compute_units() * per_cu;
+    const int blocks = ntiles < slots ? ntiles : slots;
+    kern<<<dim3(blocks), dim3(NW * 64), lds, stream>>>(x, M, codes, scales, zeros, bias, N, K, y);
+    return hipGetLastError();
+}
+
 template <int G>
 hipError_t launch_gemv_g(const uint16_t *x, int M, const uint8_t *codes,
                          const uint16_t *scales, const uint16_t *zeros,
@@ -386,16 +451,11 @@ hipError_t launch_gemv_g(const uint16_t *x, int M, const uint8_t *codes,
                          hipStream_t stream) {
     const int ntiles = (N + 15) / 16;
     const int kr = (K + 127) / 128 * 128;
-    const dim3 block(GV_WAVES * 64);
     if (M <= GV_STREAM_MAX_M && static_cast<int64_t>(M) * kr <= GV_X_ELEMS) {
-        // two resident blocks per compute unit, each streaming several tiles
-        const int blocks = ntiles < GV_STREAM_BLOCKS ? ntiles : GV_STREAM_BLOCKS;
-        gemv_stream_kernel<G, GV_WAVES><<<dim3(blocks), block, 0, stream>>>(
-            x, M, codes, scales, zeros, bias, N, K, y);
-    } else {
-        gemv_phased_kernel<G, GV_WAVES><<<dim3(ntiles), block, 0, stream>>>(
-            x, M, codes, scales, zeros, bias, N, K, y);
+        return launch_stream<G>(x, M, codes, scales, zeros, bias, N, K, y, stream);
     }
+    gemv_phased_kernel<G, GV_WAVES><<<dim3(ntiles), dim3(GV_WAVES * 64), 0, stream>>>(
+        x, M, codes, scales, zeros, bias, N, K, y);
     return hipGetLastError();
 }
 

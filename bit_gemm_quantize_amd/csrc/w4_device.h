@@ -66,6 +66,18 @@ __device__ __forceinline__ void group_minmax(float &mn, float &mx) {
     }
 }
 
+// Sum across aligned lane groups of 4, 8 or 16 lanes (every lane of the
+// group receives the group's sum).
+template <int LANES>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(LANES == 4 || LANES == 8 || LANES == 16, "group lanes");
+    v += dpp_f32<DPP_QUAD_XOR1>(v);
+    v += dpp_f32<DPP_QUAD_XOR2>(v);
+    if constexpr (LANES >= 8) v += dpp_f32<DPP_ROW_HALF_MIRROR>(v);
+    if constexpr (LANES >= 16) v += dpp_f32<DPP_ROW_MIRROR>(v);
+    return v;
+}
+
 // ----------------------------------------------------------- code unpack
 // (a & mask) | c in one VALU op. gfx9 VOP3 takes no literal operands and at
 // most one scalar operand, so the mask comes in an SGPR and c in a VGPR.
