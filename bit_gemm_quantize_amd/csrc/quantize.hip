@@ -16,13 +16,14 @@
 //
 // Exactness: the scale uses a correctly rounded binary32 divide (built with
 // correctly rounded division; no fp contraction in this file). Codes use
-// t = (w - lo) * rcp(s): with s in [2^-100, 2^100] the hardware reciprocal is
-// within 1 ulp, so |t - fl((w - lo) / s)| < 4e-6 for t <= 15.06. When t is
-// farther than 2^-16 from a half-integer, rint(t) equals rint of the
-// correctly rounded quotient; otherwise (and for extreme scales) the lane
-// recomputes every element of its chunk with the true divide. On the fast
-// path 0 <= t <= 15.06 (w - lo <= hi - lo, and (hi - lo)/s <= 15 (1 + 2^-8)),
-// so rint(t) is already inside [0, 15].
+// t = w * rcp(s) - lo * rcp(s) (one fma): with s in [2^-100, 2^100] the
+// hardware reciprocal is within 1 ulp, so t is within 15.06 * 2^-21 plus the
+// rounding of lo * rcp(s) of the correctly rounded quotient. When every t of
+// the chunk is farther than that bound (with a margin) from a half-integer,
+// rint(t) equals rint of the correctly rounded quotient; otherwise (and for
+// extreme scales) the lane recomputes its chunk with the true divide. On the
+// fast path -2^-20 < t <= 15.06 ((hi - lo)/s <= 15 (1 + 2^-8)), so rint(t)
+// is already one of 0..15 (or -0).
 #pragma clang fp contract(off)
 
 #include "w4_device.h"
@@ -34,6 +35,26 @@ namespace {
 
 constexpr int QT_THREADS = 256;
 constexpr int QT_UNROLL = 2;
+
+// min / max of three floats in one VALU op. Written in asm so that the
+// compiler does not add canonicalising copies of the bit-cast inputs (all
+// inputs here are finite).
+__device__ __forceinline__ float min3f(float a, float b, float c) {
+    float d;
+    asm("v_min3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float d;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+// max(|a|, |b|, c)
+__device__ __forceinline__ float max3_abs2(float a, float b, float c) {
+    float d;
+    asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
 
 // One lane quantizes 16 consecutive elements (two 16-byte loads); a group is
 // G/16 consecutive lanes (2, 4 or 8 inside one DPP row).
@@ -50,12 +71,15 @@ __device__ __forceinline__ void quantize16(const u32x4 d0, const u32x4 d1, int64
         v[2 * i] = bf16_lo(w[i]);
         v[2 * i + 1] = bf16_hi(w[i]);
     }
-    float mn = fminf(v[0], v[1]), mx = fmaxf(v[0], v[1]);
+    float mn = min3f(v[0], v[1], v[2]);
+    float mx = max3f(v[0], v[1], v[2]);
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) {
-        mn = fminf(mn, fminf(v[i], v[i + 1]));
-        mx = fmaxf(mx, fmaxf(v[i], v[i + 1]));
+    for (int i = 3; i < 15; i += 2) {
+        mn = min3f(mn, v[i], v[i + 1]);
+        mx = max3f(mx, v[i], v[i + 1]);
     }
+    mn = fminf(mn, v[15]);
+    mx = fmaxf(mx, v[15]);
     if constexpr (LPG >= 2) {
         mn = fminf(mn, dpp_f32<DPP_QUAD_XOR1>(mn));
         mx = fmaxf(mx, dpp_f32<DPP_QUAD_XOR1>(mx));
@@ -78,23 +102,32 @@ __device__ __forceinline__ void quantize16(const u32x4 d0, const u32x4 d1, int64
 
     uint32_t out0 = 0, out1 = 0;
     if (s != 0.0f) {
+        // Fast path: t = w * r + c with r = rcp(s), c = -lo * r. Its error
+        // against fl(fl(w - lo) / s) is below 15.06 * 2^-21 + |c| * 2^-23, so
+        // when every t is farther than 2^-16 + |c| * 2^-22 from a
+        // half-integer, rint(t) is the exact code. Otherwise (or for
+        // extreme scales) the chunk is redone with the true divide.
         const float r = __builtin_amdgcn_rcpf(s);
-        bool exact = !(s >= 0x1p-100f && s <= 0x1p100f);
+        const float cst = -lo * r;
+        const bool extreme = !(s >= 0x1p-100f && s <= 0x1p100f);
+        const float margin = 0.5f - (0x1p-16f + fabsf(cst) * 0x1p-22f);
         float q[16];
+        float dmax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float t = (v[i] - lo) * r;
-            q[i] = __builtin_rintf(t);
-            // t within 2^-16 of a half-integer: the reciprocal may have
-            // decided the rounding; redo the chunk with the true divide.
-            exact |= fabsf(t - q[i]) > 0.5f - 0x1p-16f;
+        for (int i = 0; i < 16; i += 2) {
+            const float t0 = fmaf(v[i], r, cst);
+            const float t1 = fmaf(v[i + 1], r, cst);
+            q[i] = __builtin_rintf(t0);
+            q[i + 1] = __builtin_rintf(t1);
+            dmax = max3_abs2(t0 - q[i], t1 - q[i + 1], dmax);
         }
-        if (exact) {
+        if (extreme || !(dmax < margin)) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 q[i] = fminf(fmaxf(__builtin_rintf((v[i] - lo) / s), 0.0f), 15.0f);
         }
-        // bytes q[2j] + 16 q[2j+1] (exact small integers), four per dword
+        // bytes q[2j] + 16 q[2j+1] (exact small integers), four per dword;
+        // a fast-path q may be -0 (t a hair below 0), which converts to 0
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             out0 = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(16.0f, q[2 * j + 1], q[2 * j]), j, out0);
@@ -102,37 +135,48 @@ __device__ __forceinline__ void quantize16(const u32x4 d0, const u32x4 d1, int64
         }
     }
     __builtin_nontemporal_store(u32x2{out0, out1}, codes + c);
-    if ((c & (LPG - 1)) == 0) {
-        const int64_t grp = c / LPG;
-        scales[grp] = static_cast<uint16_t>(sb);
-        zeros[grp] = static_cast<uint16_t>(zb);
-    }
+    // Every lane of the group stores the group's (identical) scale and
+    // zero-point: unconditional stores keep the number of outstanding memory
+    // operations fixed, so the loop waits only for the loads it needs.
+    const int64_t grp = c / LPG;
+    scales[grp] = static_cast<uint16_t>(sb);
+    zeros[grp] = static_cast<uint16_t>(zb);
 }
 
 template <int G>
 __global__ __launch_bounds__(QT_THREADS) void quantize_kernel(
     const u32x4 *__restrict__ W, int64_t nchunk, u32x2 *__restrict__ codes,
     uint16_t *__restrict__ scales, uint16_t *__restrict__ zeros) {
-    // nchunk counts 16-element chunks. Every chunk of a group shares the
-    // in/out-of-range decision: nchunk and the grid stride are multiples of
-    // the lanes per group.
+    // nchunk counts 16-element chunks; a thread takes chunks c, c + stride,
+    // ... and loads the next one before quantizing the current one. Every
+    // chunk of a group shares the in/out-of-range decision (nchunk and the
+    // stride are multiples of the lanes per group). Loads use a clamped
+    // index so they are never predicated.
     const int64_t stride = static_cast<int64_t>(gridDim.x) * QT_THREADS;
-    for (int64_t base = static_cast<int64_t>(blockIdx.x) * QT_THREADS + threadIdx.x;
-         base < nchunk; base += stride * QT_UNROLL) {
-        u32x4 d[QT_UNROLL][2];
-#pragma unroll
-        for (int u = 0; u < QT_UNROLL; ++u) {
-            const int64_t c = base + u * stride;
-            if (c < nchunk) {
-                d[u][0] = __builtin_nontemporal_load(W + 2 * c);
-                d[u][1] = __builtin_nontemporal_load(W + 2 * c + 1);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < QT_UNROLL; ++u) {
-            const int64_t c = base + u * stride;
-            if (c < nchunk) quantize16<G>(d[u][0], d[u][1], c, codes, scales, zeros);
-        }
+    const int64_t last = nchunk - 1;
+    int64_t c = static_cast<int64_t>(blockIdx.x) * QT_THREADS + threadIdx.x;
+    if (c >= nchunk) return;
+    u32x4 a0, a1, b0, b1;
+    auto load = [&](u32x4 &d0, u32x4 &d1, int64_t i) {
+        const int64_t il = i < last ? i : last;
+        d0 = __builtin_nontemporal_load(W + 2 * il);
+        d1 = __builtin_nontemporal_load(W + 2 * il + 1);
+    };
+    // The first chunk is peeled so that the loop is entered, and re-entered,
+    // with the same operations outstanding (the next chunk's loads, then the
+    // current chunk's stores): the waits inside stay exact.
+    load(a0, a1, c);
+    int64_t c1 = c + stride;
+    load(b0, b1, c1);
+    quantize16<G>(a0, a1, c, codes, scales, zeros);
+    while (c1 < nchunk) {
+        const int64_t c2 = c1 + stride;
+        load(a0, a1, c2);
+        quantize16<G>(b0, b1, c1, codes, scales, zeros);
+        if (c2 >= nchunk) break;
+        c1 = c2 + stride;
+        load(b0, b1, c1);
+        quantize16<G>(a0, a1, c2, codes, scales, zeros);
     }
 }
 
