@@ -114,6 +114,17 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     }
     __syncthreads();
 
+    // deferred group epilogue: acc += s * acc_g + (z - 128 s) * xsum_g
+    bool pending = false;
+    float sv[4], zz[4];
+    auto epilogue = [&](int mt) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[mt][nt][i] = fmaf(sv[nt], accg[mt][nt][i], fmaf(zz[nt], xsg[mt][i], acc[mt][nt][i]));
+    };
+
     for (int kt = 0; kt < nstages; ++kt) {
         const int cur = kt & 1;
         const bool more = kt + 1 < nstages;
@@ -141,26 +152,26 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
                 unpack8_bias128(w, u, uc);
                 b[nt] = as_bf16x8(u[0], u[1], u[2], u[3]);
             }
+            // The epilogue of the previous group runs here, one m-tile at a
+            // time, while the MFMAs of the previous m-tile are in flight: it
+            // reads accg / xsg of m-tile mt just before this slice's first
+            // MFMAs overwrite them.
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
+                if (pending) epilogue(mt);
                 xsg[mt] = mfma16x16x32(a[mt], ones, first ? zero4 : xsg[mt]);
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt)
                     accg[mt][nt] = mfma16x16x32(a[mt], b[nt], first ? zero4 : accg[mt][nt]);
             }
+            pending = last;
             if (last) {
                 const int h = (G == 32) ? sl : 0;
 #pragma unroll
                 for (int nt = 0; nt < 4; ++nt) {
                     const uint32_t szv = SZ[cur][h][wn * 64 + nt * 16 + nl];
-                    const float sv = bf16_lo(szv);
-                    const float zz = fmaf(-128.0f, sv, bf16_hi(szv));
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            acc[mt][nt][i] = fmaf(sv, accg[mt][nt][i],
-                                                  fmaf(zz, xsg[mt][i], acc[mt][nt][i]));
+                    sv[nt] = bf16_lo(szv);
+                    zz[nt] = fmaf(-128.0f, sv[nt], bf16_hi(szv));
                 }
             }
         }
@@ -170,6 +181,11 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
             SZ[cur ^ 1][sz_h][sz_row] = sz_nxt;
         }
         __syncthreads();
+    }
+
+    if (pending) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) epilogue(mt);
     }
 
     // Store: lane holds rows 4*kb + i of each 16 x 16 tile, column nl.
