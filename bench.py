@@ -27,6 +27,14 @@ METRIC = ("W4A16 linear: achieved HBM GB/s (M=1) and TFLOP/s (M=2048), "
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 ROTATE_BYTES = 1 << 30          # rotate weight copies over >= 1 GiB
+CSRC = os.path.join(ROOT, "bit_gemm_quantize_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+# device sources each kernel is built from (a change voids its counters)
+KERNEL_SOURCES = {
+    "quantize_kernel": ["quantize.hip", "w4_device.h", "w4_launch.h"],
+    "gemv_stream_kernel": ["gemv.hip", "w4_device.h", "w4_launch.h"],
+    "gemm_kernel": ["gemm.hip", "w4_device.h", "w4_launch.h"],
+}
 
 
 def log(msg):
@@ -39,6 +47,49 @@ def quant_bytes(N, K, G):
 
 def linear_bytes(M, N, K, G):
     return N * K // 2 + 4 * N * K // G + 2 * M * K + 2 * M * N
+
+
+def kernel_source_hash(kernel):
+    """sha256 over the device sources a kernel is compiled from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this kernel (FETCH_SIZE + WRITE_SIZE, each scaled by the factor the same
+    counter gives for a plain device copy of known size). Returns None when
+    no summary exists or the kernel's sources changed since it was taken.
+    The summary carries one machine-readable line:
+      traffic: kernel=<name> sources_sha256=<hex> fetch_bytes=<B> write_bytes=<B>
+    """
+    try:
+        names = sorted(os.listdir(PROFILES))
+    except OSError:
+        return None
+    want = kernel_source_hash(kernel)
+    for n in names:
+        if not n.endswith((".md", ".txt")):
+            continue
+        with open(os.path.join(PROFILES, n)) as fh:
+            for line in fh:
+                line = line.strip().strip("`")
+                if not line.startswith("traffic:"):
+                    continue
+                kv = dict(t.split("=", 1) for t in line[len("traffic:"):].split() if "=" in t)
+                if kv.get("kernel") != kernel:
+                    continue
+                if kv.get("sources_sha256") != want:
+                    return None
+                return {"fetch_bytes_per_launch": float(kv["fetch_bytes"]),
+                        "write_bytes_per_launch": float(kv["write_bytes"]),
+                        "bytes_per_launch": float(kv["fetch_bytes"]) + float(kv["write_bytes"]),
+                        "source": f"profiles/{n}"}
+    return None
 
 
 def graph_of(torch, fns):
@@ -128,7 +179,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "step", "gemv", "gemm", "quantize"],
+    ap.add_argument("--only", choices=["all", "step", "gemv", "gemm", "quantize", "copy"],
                     default="all", help="restrict to one part (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -222,6 +273,7 @@ def main():
             del g
         out["quantize"] = {
             "kernel": "quantize_kernel<128>", "bound": "hbm",
+            "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
             "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
             "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_per_set": tot_b, "set_us": round(tot_ms * 1e3, 3),
@@ -266,7 +318,8 @@ def main():
         set_ms = time_graphs(torch, [g], max(2, reps // 2)) / n_g
         del g
         out["gemv_m1"] = {
-            "kernel": "gemv_kernel<128,8>", "bound": "hbm",
+            "kernel": "gemv_stream_kernel<128, 8>", "bound": "hbm",
+            "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
             "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
             "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_per_set": tot_b,
@@ -300,6 +353,7 @@ def main():
             del g, x, c, s_, z, y
         out["gemm_m2048"] = {
             "kernel": "gemm_kernel<128>", "bound": "mfma",
+            "avg_launch_us": round(tot_ms * 1e3 / len(glayers), 2),
             "achieved_TFLOPs": round(tot_f / (tot_ms * 1e-3) / 1e12, 1),
             "frac": round(tot_f / (tot_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "flops_per_set": tot_f,
@@ -308,13 +362,20 @@ def main():
         }
 
     # ---- achievable-bandwidth reference: torch's own device copy ----------
-    if args.only == "all":
+    # The same buffers calibrate the HBM byte counters: an elementwise
+    # bitwise_not is a plain kernel that reads 1 GiB and writes 1 GiB per
+    # launch (the device copy above may run as a runtime blit).
+    if args.only in ("all", "copy"):
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         g = graph_of(torch, [lambda: b.copy_(a)])
         ms = time_graphs(torch, [g], 20)
+        del g
+        g = graph_of(torch, [lambda: torch.bitwise_not(a, out=b)])
+        ms_not = time_graphs(torch, [g], 20)
         out["hbm_reference"] = {"what": "torch device copy of 1 GiB (read + write)",
-                                "GBps": round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1)}
+                                "GBps": round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1),
+                                "elementwise_GBps": round(2 * (1 << 30) / (ms_not * 1e-3) / 1e9, 1)}
         del a, b, g
 
     # ---- report ------------------------------------------------------------
@@ -328,18 +389,29 @@ def main():
         if q_ms >= g_ms:
             b = sum(quant_bytes(N, K, G) for N, K in layers.values())
             a_gbs = b / (q_ms * 1e-3) / 1e9
-            kname = "quantize_kernel<128>"
+            kname = "quantize_kernel"
             nl = len(q_ms_launch)
         else:
             b = sum(linear_bytes(1, N, K, G) for N, K in layers.values())
             a_gbs = b / (g_ms * 1e-3) / 1e9
-            kname = "gemv_kernel<128,8>"
+            kname = "gemv_stream_kernel"
             nl = len(g_ms_launch)
+        tr = measured_traffic(kname)
         roofline = {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(a_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": kname,
+                    "unit": "GB/s", "frac": round(a_gbs / HBM_PEAK_GBS, 4),
+                    "traffic": round(tr["bytes_per_launch"]) if tr else None,
+                    "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                    "copy-calibrated)",
+                    "traffic_detail": tr,
+                    "kernel": kname + "<128>",
                     "avg_launch_us": round((q_ms if q_ms >= g_ms else g_ms) * 1e3 / nl, 3),
                     "bytes_per_launch_avg": b // nl}
+
+    for comp, kern in (("quantize", "quantize_kernel"), ("gemv_m1", "gemv_stream_kernel"),
+                       ("gemm_m2048", "gemm_kernel")):
+        if comp in out:
+            tr = measured_traffic(kern)
+            out[comp]["traffic_bytes_per_launch"] = round(tr["bytes_per_launch"]) if tr else None
 
     cpu = None
     if not args.no_cpu_baseline and args.only == "all":
