@@ -28,7 +28,8 @@ template <int G>
 __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
-    const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y) {
+    const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y,
+    int64_t tile0, int64_t ntiles) {
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][A_LD];
     __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN][B_LD];
     __shared__ uint32_t SZ[2][2][BN];          // (s | z << 16) per group end
@@ -38,8 +39,24 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int nl = lane & 15, kb = lane >> 4;
-    const int m0 = blockIdx.y * BM;
-    const int n0 = blockIdx.x * BN;
+    // Tile order. Workgroups go to the 8 XCDs round-robin (block b to XCD
+    // b % 8), each XCD with its own L2. Block b is given tile t so that each
+    // XCD runs one contiguous run of the tile order, and the tile order walks
+    // groups of up to 4 m-tiles, n-tile by n-tile: the blocks an XCD runs at
+    // once (64 of them) then share 4 row tiles of x and 16 tiles of codes,
+    // which its L2 keeps while they move along K together.
+    int m0, n0;
+    {
+        const int64_t T = ntiles, b = blockIdx.x;
+        const int64_t xcd = b & 7, j = b >> 3;
+        const int64_t t = tile0 + xcd * (T >> 3) + min(xcd, T & 7) + j;
+        const int64_t mtiles = (M + BM - 1) / BM, ntl = (N + BN - 1) / BN;
+        const int64_t gm = min<int64_t>(4, mtiles);
+        const int64_t grp = t / (gm * ntl), r = t - grp * gm * ntl;
+        const int64_t gsz = min(gm, mtiles - grp * gm);
+        m0 = static_cast<int>((grp * gm + r % gsz) * BM);
+        n0 = static_cast<int>((r / gsz) * BN);
+    }
     const int ngroups = K / G;
     const int nstages = (K + KS - 1) / KS;
     const int64_t code_ld = K >> 1;
@@ -69,8 +86,8 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
             ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + min(k0, K - 8 - col));
         }
         // k = min(k0 + 32 * half, K - 32)
-        rb = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-            b_src + min(k0, K - 32 - b_half * 32) / 2));
+        // (cached: each code tile is read by every m-tile)
+        rb = *reinterpret_cast<const u32x4 *>(b_src + min(k0, K - 32 - b_half * 32) / 2);
     };
     auto store_stage = [&](int buf, const u32x4 (&ra)[4], const u32x4 &rb) {
 #pragma unroll
@@ -212,17 +229,24 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *codes,
                        const uint16_t *scales, const uint16_t *zeros,
                        const uint16_t *bias, int64_t N, int64_t K, int G,
                        uint16_t *y, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>((N + BN - 1) / BN),
-                    static_cast<unsigned>((M + BM - 1) / BM));
-    const dim3 block(THREADS);
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-    switch (G) {
-    case 32: gemm_kernel<32><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, bias, n, k, y); break;
-    case 64: gemm_kernel<64><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, bias, n, k, y); break;
-    case 128: gemm_kernel<128><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, bias, n, k, y); break;
-    default: return hipErrorInvalidValue;
+    // one launch per 2^22 tiles keeps blocks x threads below 2^32
+    constexpr int64_t kMaxTiles = int64_t(1) << 22;
+    for (int64_t t0 = 0; t0 < tiles; t0 += kMaxTiles) {
+        const int64_t nt = min(kMaxTiles, tiles - t0);
+        const dim3 grid(static_cast<unsigned>(nt));
+        const dim3 block(THREADS);
+        switch (G) {
+        case 32: gemm_kernel<32><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
+        case 64: gemm_kernel<64><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
+        case 128: gemm_kernel<128><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
+        default: return hipErrorInvalidValue;
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 } // namespace w4
