@@ -12,6 +12,8 @@
 // bf16 MFMAs into a per-group accumulator; an MFMA against an all-ones B
 // gives the group sums of x in the same layout. At the end of a group:
 //   acc += s * acc_g + (z - 128 s) * xsum_g        (float32)
+#include <type_traits>
+
 #include "w4_device.h"
 #include "w4_launch.h"
 
@@ -20,9 +22,11 @@ namespace w4 {
 namespace {
 
 constexpr int BM = 128, BN = 128, KS = 64;
-constexpr int A_LD = KS + 8;                   // bf16 elements per LDS row
-constexpr int B_LD = KS / 2 + 16;              // bytes per LDS code row
+constexpr int LD = KS + 8;                     // bf16 elements per LDS row
 constexpr int THREADS = 256;
+
+template <int V>
+using IC = std::integral_constant<int, V>;
 
 template <int G>
 __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
@@ -30,8 +34,10 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y,
     int64_t tile0, int64_t ntiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][A_LD];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN][B_LD];
+    // x tile and the expanded code tile (bf16 128 + q), rows padded by 16
+    // bytes against bank conflicts; both double buffered.
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LD];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LD];
     __shared__ uint32_t SZ[2][2][BN];          // (s | z << 16) per group end
 
     const int tid = threadIdx.x;
@@ -39,6 +45,10 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     const int wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int nl = lane & 15, kb = lane >> 4;
+    const int ngroups = K / G;
+    const int nstages = (K + KS - 1) / KS;
+    const int64_t code_ld = K >> 1;
+
     // Tile order. Workgroups go to the 8 XCDs round-robin (block b to XCD
     // b % 8), each XCD with its own L2. Block b is given tile t so that each
     // XCD runs one contiguous run of the tile order, and the tile order walks
@@ -57,15 +67,12 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
         m0 = static_cast<int>((grp * gm + r % gsz) * BM);
         n0 = static_cast<int>((r / gsz) * BN);
     }
-    const int ngroups = K / G;
-    const int nstages = (K + KS - 1) / KS;
-    const int64_t code_ld = K >> 1;
 
-    // Global -> LDS staging. Loads are unconditional with clamped addresses:
-    // rows past M or N only feed outputs that are never stored, and a stage
-    // past K (K % 64 == 32) is never read.
+    // Global -> register -> LDS staging. Loads are unconditional with clamped
+    // addresses: rows past M or N only feed outputs that are never stored,
+    // and a stage past K (K % 64 == 32) is never read.
     // x: 128 rows x 8 pieces of 16 B; thread handles pieces tid + 256 i.
-    // codes: 128 rows x 2 pieces of 16 B; thread handles piece tid.
+    // codes: 128 rows x 2 pieces of 16 B (32 codes); thread handles piece tid.
     const uint16_t *a_src[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -85,10 +92,12 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
             // k = min(k0 + col, K - 8): stays inside the row
             ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + min(k0, K - 8 - col));
         }
-        // k = min(k0 + 32 * half, K - 32)
-        // (cached: each code tile is read by every m-tile)
+        // k = min(k0 + 32 * half, K - 32); cached: every m-tile reads it
         rb = *reinterpret_cast<const u32x4 *>(b_src + min(k0, K - 32 - b_half * 32) / 2);
     };
+    // The codes are expanded once per block here, on their way into LDS, to
+    // the exact bf16 integers 128 + q (natural k order, like x).
+    const Unpack128 uc = unpack128_consts();
     auto store_stage = [&](int buf, const u32x4 (&ra)[4], const u32x4 &rb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -96,7 +105,13 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
             const int row = idx >> 3, col = (idx & 7) * 8;
             *reinterpret_cast<u32x4 *>(&As[buf][row][col]) = ra[i];
         }
-        *reinterpret_cast<u32x4 *>(&Bs[buf][b_row][b_half * 16]) = rb;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            uint32_t u[4];
+            unpack8_bias128(rb[w], u, uc);
+            *reinterpret_cast<u32x4 *>(&Bs[buf][b_row][b_half * 32 + 8 * w]) =
+                u32x4{u[0], u[1], u[2], u[3]};
+        }
     };
 
     // Scales and zero-points of the groups that end inside a stage go
@@ -113,14 +128,17 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
         return static_cast<uint32_t>(scales[g]) | (static_cast<uint32_t>(zeros[g]) << 16);
     };
 
+    // accg / xsg / sv / zz start at zero so that the deferred epilogue at the
+    // first slice of the first group adds nothing.
     f32x4 acc[4][4], accg[4][4], xsg[4];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+        xsg[i] = zero4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = zero4;
+        for (int j = 0; j < 4; ++j) acc[i][j] = accg[i][j] = zero4;
+    }
     const bf16x8 ones = bf16x8_ones();
-    const Unpack128 uc = unpack128_consts();
 
     {
         u32x4 ra[4], rb;
@@ -132,8 +150,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     __syncthreads();
 
     // deferred group epilogue: acc += s * acc_g + (z - 128 s) * xsum_g
-    bool pending = false;
-    float sv[4], zz[4];
+    float sv[4] = {0.f, 0.f, 0.f, 0.f}, zz[4] = {0.f, 0.f, 0.f, 0.f};
     auto epilogue = [&](int mt) {
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
@@ -142,68 +159,90 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
                 acc[mt][nt][i] = fmaf(sv[nt], accg[mt][nt][i], fmaf(zz[nt], xsg[mt][i], acc[mt][nt][i]));
     };
 
-    for (int kt = 0; kt < nstages; ++kt) {
-        const int cur = kt & 1;
+    // Slice sl of a stage held in LDS buffer buf; par is the stage's parity
+    // for G = 128 (a group spans two stages). Where groups start and end is
+    // known at compile time: G = 128 spans a pair of stages, G = 64 a stage,
+    // G = 32 a slice.
+    auto slice = [&](int buf, auto par_c, auto sl_c) {
+        constexpr int par = decltype(par_c)::value;
+        constexpr int sl = decltype(sl_c)::value;
+        constexpr bool first = G == 128 ? (par == 0 && sl == 0) : (G == 64 ? sl == 0 : true);
+        constexpr bool last = G == 128 ? (par == 1 && sl == 1) : (G == 64 ? sl == 1 : true);
+        bf16x8 a[4], b[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            a[mt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+                &As[buf][wm * 64 + mt * 16 + nl][sl * 32 + kb * 8]));
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+            b[nt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(
+                &Bs[buf][wn * 64 + nt * 16 + nl][sl * 32 + kb * 8]));
+        // The epilogue of the previous group runs in the first slice of the
+        // next one, one m-tile at a time, while the MFMAs of the previous
+        // m-tile are in flight: it reads accg / xsg of m-tile mt just before
+        // this slice's first MFMAs overwrite them.
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            if constexpr (first) {
+                epilogue(mt);
+                // Pin the order: the updated acc is materialised here, and
+                // this m-tile's MFMAs (which start new accumulators) take an
+                // operand that passes through the same point, so the old
+                // accumulators die before the new ones are written.
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) asm volatile("" : "+v"(acc[mt][nt]));
+                asm volatile("" : "+v"(a[mt]));
+            }
+            xsg[mt] = mfma16x16x32(a[mt], ones, first ? zero4 : xsg[mt]);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt)
+                accg[mt][nt] = mfma16x16x32(a[mt], b[nt], first ? zero4 : accg[mt][nt]);
+        }
+        if constexpr (last) {
+            constexpr int h = (G == 32) ? sl : 0;
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                const uint32_t szv = SZ[buf][h][wn * 64 + nt * 16 + nl];
+                sv[nt] = bf16_lo(szv);
+                zz[nt] = fmaf(-128.0f, sv[nt], bf16_hi(szv));
+            }
+        }
+    };
+
+    auto stage = [&](int buf, auto par_c, int kt) {
         const bool more = kt + 1 < nstages;
         u32x4 ra[4], rb;
         load_stage(more ? kt + 1 : kt, ra, rb);
         const uint32_t sz_nxt = load_sz(more ? kt + 1 : kt);
-
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-            const int k0 = kt * KS + sl * 32;
-            if (k0 >= K) break;
-            const bool first = (k0 % G) == 0;
-            const bool last = ((k0 + 32) % G) == 0;
-            bf16x8 a[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                a[mt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                    &As[cur][wm * 64 + mt * 16 + nl][sl * 32 + kb * 8]));
-            bf16x8 b[4];
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt) {
-                const uint32_t w = *reinterpret_cast<const uint32_t *>(
-                    &Bs[cur][wn * 64 + nt * 16 + nl][sl * 16 + kb * 4]);
-                uint32_t u[4];
-                unpack8_bias128(w, u, uc);
-                b[nt] = as_bf16x8(u[0], u[1], u[2], u[3]);
-            }
-            // The epilogue of the previous group runs here, one m-tile at a
-            // time, while the MFMAs of the previous m-tile are in flight: it
-            // reads accg / xsg of m-tile mt just before this slice's first
-            // MFMAs overwrite them.
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                if (pending) epilogue(mt);
-                xsg[mt] = mfma16x16x32(a[mt], ones, first ? zero4 : xsg[mt]);
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt)
-                    accg[mt][nt] = mfma16x16x32(a[mt], b[nt], first ? zero4 : accg[mt][nt]);
-            }
-            pending = last;
-            if (last) {
-                const int h = (G == 32) ? sl : 0;
-#pragma unroll
-                for (int nt = 0; nt < 4; ++nt) {
-                    const uint32_t szv = SZ[cur][h][wn * 64 + nt * 16 + nl];
-                    sv[nt] = bf16_lo(szv);
-                    zz[nt] = fmaf(-128.0f, sv[nt], bf16_hi(szv));
-                }
-            }
+        __builtin_amdgcn_sched_barrier(0);      // issue the loads first
+        slice(buf, par_c, IC<0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (G == 32) {
+            if (kt * KS + 32 < K) slice(buf, par_c, IC<1>{});   // K % 64 == 32: half stage
+        } else {
+            slice(buf, par_c, IC<1>{});                          // K % 64 == 0
         }
-
+        __builtin_amdgcn_sched_barrier(0);
         if (more) {
-            store_stage(cur ^ 1, ra, rb);
-            SZ[cur ^ 1][sz_h][sz_row] = sz_nxt;
+            store_stage(buf ^ 1, ra, rb);
+            SZ[buf ^ 1][sz_h][sz_row] = sz_nxt;
         }
         __syncthreads();
+    };
+
+    if constexpr (G == 128) {
+        // K is a multiple of 128: the stage count is even
+        for (int kt = 0; kt < nstages; kt += 2) {
+            stage(0, IC<0>{}, kt);
+            stage(1, IC<1>{}, kt + 1);
+        }
+    } else {
+        for (int kt = 0; kt < nstages; ++kt) stage(kt & 1, IC<0>{}, kt);
     }
 
-    if (pending) {
+    // the last group ends with the last slice
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) epilogue(mt);
-    }
+    for (int mt = 0; mt < 4; ++mt) epilogue(mt);
 
     // Store: lane holds rows 4*kb + i of each 16 x 16 tile, column nl.
 #pragma unroll
