@@ -5,13 +5,16 @@
 // ("Optimum Quanto": wide accumulation, then dequantization; bias in float).
 //
 // Block tile 128 (m) x 128 (n), four waves in a 2 x 2 grid, 64 x 64 each.
-// K advances in stages of 64 (two 32-wide slices), double buffered in LDS:
-// the x tile is kept as bf16 (rows padded by 16 bytes against bank
-// conflicts) and the code tile as packed nibbles. For each slice a wave
-// expands its codes to the exact bf16 integers 128 + q and runs 16x16x32
-// bf16 MFMAs into a per-group accumulator; an MFMA against an all-ones B
-// gives the group sums of x in the same layout. At the end of a group:
-//   acc += s * acc_g + (z - 128 s) * xsum_g        (float32)
+// K advances in stages of 64 (two 32-wide slices), double buffered in LDS.
+// The x tile is copied global -> LDS directly (16 bytes per lane, XOR
+// swizzled rows); the code tile goes through registers and is expanded on
+// its way into LDS to the exact bf16 integers 128 + q. Each slice runs
+// 16x16x32 bf16 MFMAs into a per-group accumulator, plus one MFMA against an
+// all-ones B for the group sums of x in the same layout. After a group, in
+// float32:
+//   acc += s * acc_g + (z - 128 s) * xsum_g
+// (128 + q is exact in bf16 and the MFMA accumulates exactly-representable
+// products in float32, so the only rounding is the float32 accumulation.)
 #include <type_traits>
 
 #include "w4_device.h"
@@ -34,11 +37,12 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y,
     int64_t tile0, int64_t ntiles) {
-    // x tile and the expanded code tile (bf16 128 + q), rows padded by 16
-    // bytes against bank conflicts; both double buffered.
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LD];
+    // x tile (swizzled, see below) and the expanded code tile (bf16 128 + q,
+    // rows padded by 16 bytes against bank conflicts); both double buffered.
+    __shared__ __attribute__((aligned(1024))) uint16_t A0[BM * KS];
+    __shared__ __attribute__((aligned(1024))) uint16_t A1[BM * KS];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LD];
-    __shared__ uint32_t SZ[2][2][BN];          // (s | z << 16) per group end
+    __shared__ uint16_t S16[2][2][BN], Z16[2][2][BN];   // s, z per group end
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -68,29 +72,42 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
         n0 = static_cast<int>((r / gsz) * BN);
     }
 
-    // Global -> register -> LDS staging. Loads are unconditional with clamped
-    // addresses: rows past M or N only feed outputs that are never stored,
-    // and a stage past K (K % 64 == 32) is never read.
-    // x: 128 rows x 8 pieces of 16 B; thread handles pieces tid + 256 i.
-    // codes: 128 rows x 2 pieces of 16 B (32 codes); thread handles piece tid.
-    const uint16_t *a_src[4];
+    // Staging. Loads are unconditional with clamped addresses: rows past M
+    // or N only feed outputs that are never stored, and a stage past K
+    // (K % 64 == 32) is never read.
+    // x goes straight to LDS (16 bytes per lane per load): load i of wave w
+    // fills rows 8 (4w + i) .. +8, lane l row + l / 8, 16-byte slot l % 8,
+    // which holds k-piece (l % 8) ^ (row % 8) (XOR swizzle against bank
+    // conflicts of the fragment reads).
+    // codes: 128 rows x 2 pieces of 16 B (32 codes); thread tid loads piece
+    // tid into registers.
+    const int a_r8 = lane >> 3;
+    const int a_piece = (lane & 7) ^ (a_r8 & 7);
+    uint32_t a_row[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int idx = tid + THREADS * i;
-        const int row = idx >> 3, col = (idx & 7) * 8;
-        a_src[i] = x + static_cast<int64_t>(min(m0 + row, M - 1)) * K + col;
-    }
+    for (int i = 0; i < 4; ++i)
+        a_row[i] = static_cast<uint32_t>(min(m0 + (wave * 4 + i) * 8 + a_r8, M - 1));
     const int b_row = tid >> 1, b_half = tid & 1;
     const uint8_t *b_src = codes + static_cast<int64_t>(min(n0 + b_row, N - 1)) * code_ld +
                            b_half * 16;
 
-    auto load_stage = [&](int kt, u32x4 (&ra)[4], u32x4 &rb) {
+    // LDS byte addresses of the two x buffers
+    const uint32_t a_lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) uint16_t *)A0));
+    const uint32_t a_lds1 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) uint16_t *)A1));
+    auto load_stage = [&](int kt, int dbuf, u32x4 &rb) {
         const int k0 = kt * KS;
+        const uint32_t k = static_cast<uint32_t>(min(k0 + a_piece * 8, K - 8));
+        const uint32_t base = __builtin_amdgcn_readfirstlane((dbuf ? a_lds1 : a_lds0) + wave * 4 * 1024);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int col = ((tid + THREADS * i) & 7) * 8;
-            // k = min(k0 + col, K - 8): stays inside the row
-            ra[i] = *reinterpret_cast<const u32x4 *>(a_src[i] + min(k0, K - 8 - col));
+            const uint16_t *g = x + (static_cast<uint64_t>(a_row[i]) * static_cast<uint32_t>(K) + k);
+            const uint32_t l = base + i * 1024;
+            asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                         :
+                         : "v"(g), "s"(l)
+                         : "memory", "m0");
         }
         // k = min(k0 + 32 * half, K - 32); cached: every m-tile reads it
         rb = *reinterpret_cast<const u32x4 *>(b_src + min(k0, K - 32 - b_half * 32) / 2);
@@ -98,13 +115,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     // The codes are expanded once per block here, on their way into LDS, to
     // the exact bf16 integers 128 + q (natural k order, like x).
     const Unpack128 uc = unpack128_consts();
-    auto store_stage = [&](int buf, const u32x4 (&ra)[4], const u32x4 &rb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int idx = tid + THREADS * i;
-            const int row = idx >> 3, col = (idx & 7) * 8;
-            *reinterpret_cast<u32x4 *>(&As[buf][row][col]) = ra[i];
-        }
+    auto store_stage = [&](int buf, const u32x4 &rb) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             uint32_t u[4];
@@ -121,11 +132,11 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     // clamped; entries of groups that do not end are never read.
     const int sz_row = tid & (BN - 1), sz_h = tid >> 7;
     const int64_t sz_base = static_cast<int64_t>(min(n0 + sz_row, N - 1)) * ngroups;
-    auto load_sz = [&](int kt) -> uint32_t {
+    auto load_sz = [&](int kt) -> u32x2 {
         const int k_end = kt * KS + (G == 32 ? (sz_h + 1) * 32 : KS);
         // for G = 128 no group ends in even stages: k_end / G - 1 can be -1
         const int64_t g = sz_base + max(0, min(k_end / G - 1, ngroups - 1));
-        return static_cast<uint32_t>(scales[g]) | (static_cast<uint32_t>(zeros[g]) << 16);
+        return u32x2{scales[g], zeros[g]};
     };
 
     // accg / xsg / sv / zz start at zero so that the deferred epilogue at the
@@ -141,11 +152,13 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     const bf16x8 ones = bf16x8_ones();
 
     {
-        u32x4 ra[4], rb;
-        load_stage(0, ra, rb);
-        const uint32_t sz = load_sz(0);
-        store_stage(0, ra, rb);
-        SZ[0][sz_h][sz_row] = sz;
+        u32x4 rb;
+        load_stage(0, 0, rb);
+        const u32x2 sz = load_sz(0);
+        store_stage(0, rb);
+        S16[0][sz_h][sz_row] = static_cast<uint16_t>(sz[0]);
+        Z16[0][sz_h][sz_row] = static_cast<uint16_t>(sz[1]);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
 
@@ -168,11 +181,14 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
         constexpr int sl = decltype(sl_c)::value;
         constexpr bool first = G == 128 ? (par == 0 && sl == 0) : (G == 64 ? sl == 0 : true);
         constexpr bool last = G == 128 ? (par == 1 && sl == 1) : (G == 64 ? sl == 1 : true);
+        const uint16_t *Ab = buf ? A1 : A0;
         bf16x8 a[4], b[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < 4; ++mt) {
+            const int r = wm * 64 + mt * 16 + nl;
             a[mt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                &As[buf][wm * 64 + mt * 16 + nl][sl * 32 + kb * 8]));
+                Ab + r * KS + (((sl * 4 + kb) ^ (r & 7)) * 8)));
+        }
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
             b[nt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(
@@ -202,31 +218,32 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
             constexpr int h = (G == 32) ? sl : 0;
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
-                const uint32_t szv = SZ[buf][h][wn * 64 + nt * 16 + nl];
-                sv[nt] = bf16_lo(szv);
-                zz[nt] = fmaf(-128.0f, sv[nt], bf16_hi(szv));
+                const int c = wn * 64 + nt * 16 + nl;
+                sv[nt] = bf16_to_f32(S16[buf][h][c]);
+                zz[nt] = fmaf(-128.0f, sv[nt], bf16_to_f32(Z16[buf][h][c]));
             }
         }
     };
 
     auto stage = [&](int buf, auto par_c, int kt) {
         const bool more = kt + 1 < nstages;
-        u32x4 ra[4], rb;
-        load_stage(more ? kt + 1 : kt, ra, rb);
-        const uint32_t sz_nxt = load_sz(more ? kt + 1 : kt);
+        u32x4 rb;
+        // (the last stage reloads itself into the other buffer: unused)
+        load_stage(more ? kt + 1 : kt, buf ^ 1, rb);
+        const u32x2 sz_nxt = load_sz(more ? kt + 1 : kt);
         __builtin_amdgcn_sched_barrier(0);      // issue the loads first
         slice(buf, par_c, IC<0>{});
-        __builtin_amdgcn_sched_barrier(0);
         if constexpr (G == 32) {
             if (kt * KS + 32 < K) slice(buf, par_c, IC<1>{});   // K % 64 == 32: half stage
         } else {
             slice(buf, par_c, IC<1>{});                          // K % 64 == 0
         }
-        __builtin_amdgcn_sched_barrier(0);
-        if (more) {
-            store_stage(buf ^ 1, ra, rb);
-            SZ[buf ^ 1][sz_h][sz_row] = sz_nxt;
-        }
+        // (unconditional: after the last stage the other buffer is not read)
+        store_stage(buf ^ 1, rb);
+        S16[buf ^ 1][sz_h][sz_row] = static_cast<uint16_t>(sz_nxt[0]);
+        Z16[buf ^ 1][sz_h][sz_row] = static_cast<uint16_t>(sz_nxt[1]);
+        // the x tile of the next stage has landed in LDS
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
 
