@@ -32,7 +32,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # device sources each kernel is built from (a change voids its counters)
 KERNEL_SOURCES = {
     "quantize_kernel": ["quantize.hip", "w4_device.h", "w4_launch.h"],
-    "gemv_stream_kernel": ["gemv.hip", "w4_device.h", "w4_launch.h"],
+    "gemv_split_kernel": ["gemv.hip", "w4_device.h", "w4_launch.h"],
     "gemm_kernel": ["gemm.hip", "w4_device.h", "w4_launch.h"],
 }
 
@@ -318,7 +318,7 @@ def main():
         set_ms = time_graphs(torch, [g], max(2, reps // 2)) / n_g
         del g
         out["gemv_m1"] = {
-            "kernel": "gemv_stream_kernel<128, 8>", "bound": "hbm",
+            "kernel": "gemv_split_kernel<128, 8>", "bound": "hbm",
             "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
             "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
             "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -394,7 +394,7 @@ def main():
         else:
             b = sum(linear_bytes(1, N, K, G) for N, K in layers.values())
             a_gbs = b / (g_ms * 1e-3) / 1e9
-            kname = "gemv_stream_kernel"
+            kname = "gemv_split_kernel"
             nl = len(g_ms_launch)
         tr = measured_traffic(kname)
         roofline = {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,
@@ -407,7 +407,7 @@ def main():
                     "avg_launch_us": round((q_ms if q_ms >= g_ms else g_ms) * 1e3 / nl, 3),
                     "bytes_per_launch_avg": b // nl}
 
-    for comp, kern in (("quantize", "quantize_kernel"), ("gemv_m1", "gemv_stream_kernel"),
+    for comp, kern in (("quantize", "quantize_kernel"), ("gemv_m1", "gemv_split_kernel"),
                        ("gemm_m2048", "gemm_kernel")):
         if comp in out:
             tr = measured_traffic(kern)

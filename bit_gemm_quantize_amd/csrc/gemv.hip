@@ -5,26 +5,26 @@
 // ("Optimum Quanto": bf16-int4 matmul, accumulated in float32 and
 // dequantized afterwards; bias kept in float.)
 //
-// The kernel streams the packed codes once from HBM. Work split:
-//   * a block owns 16 output features (rows of the code matrix) and all of
-//     K; its 8 waves split K into contiguous runs of 128-wide chunks and
-//     combine their partial sums through LDS at the end;
-//   * x[0:M, :] is staged once per block in LDS (in phases of columns when
-//     M*K does not fit) and read from there as the MFMA A operand;
+// The codes are streamed once from HBM. Common to both kernels below:
+//   * a tile is 16 output features (rows of the code matrix); the waves that
+//     share a tile split K into runs of 128-wide chunks and add their partial
+//     sums through LDS;
 //   * per chunk, lane l (feature l%16, quarter kb = l/16) loads 16 bytes =
 //     32 codes (k = 128c + 32kb ... +32) with one 128-bit load, so a wave
-//     load covers 64 contiguous bytes of each of 16 rows; the codes, scales
-//     and zero-points of the next batch of chunks are in flight while the
-//     current batch is computed;
+//     load covers 64 contiguous bytes of each of 16 rows; the loads of the
+//     next chunks are in flight while the current ones are computed;
 //   * codes are expanded in registers to the exact bf16 integers 128 + q and
-//     fed with bf16 x to the 16x16x32 matrix-core op; M <= 16 rows of x fill
-//     the A operand (rows >= M are zero);
+//     fed with bf16 x (staged in LDS) to the 16x16x32 matrix-core op; the
+//     M <= 16 rows of x fill the A operand (rows >= M repeat row M - 1 and
+//     are never stored);
 //   * each MFMA must contract a single group, so for G = 64 / 32 the four
 //     dwords a lane holds are first exchanged across the lane quarters
 //     (permlane swaps) so that slot j of every quarter lies in one group;
-//   * a second MFMA against an all-ones B gives sum_{k in g} x[m][k] in the
-//     same lane layout; at the end of a group, in float32:
-//         acc += s * acc_g + (z - 128 s) * xsum_g.
+//   * at the end of a group, in float32:
+//         acc += s * acc_g + (z - 128 s) * xsum_g,
+//     with xsum_g = sum_{k in g} x[m][k] staged beside x (split kernel) or
+//     from a second MFMA against an all-ones B (phased kernel).
+
 #include "w4_device.h"
 #include "w4_launch.h"
 
@@ -70,10 +70,10 @@ __device__ __forceinline__ void align_groups(u32x4 &d) {
 
 constexpr int GV_WAVES = 8;              // waves per block (split of K)
 constexpr int GV_X_ELEMS = 32768;        // bf16 elements of x staged in LDS
-constexpr int GV_STREAM_MAX_M = 4;      // persistent kernel: M <= 4
-constexpr int GV_STREAM_WAVES = 8;      // persistent kernel: waves per block
-constexpr int GV_STREAM_MAX_LDS = GV_X_ELEMS * 2 + (GV_X_ELEMS / 32) * 4 * 4 +
-                                  2 * GV_STREAM_WAVES * 4 * 16 * 4;
+constexpr int GV_SPLIT_MAX_M = 4;       // split-K kernel: M <= 4
+constexpr int GV_SPLIT_WAVES = 8;       // split-K kernel: waves per block
+constexpr int GV_SPLIT_MAX_LDS = GV_X_ELEMS * 2 + (GV_X_ELEMS / 32) * GV_SPLIT_MAX_M * 4 +
+                                 2 * GV_SPLIT_WAVES * GV_SPLIT_MAX_M * 16 * 4;
 
 // Codes of U consecutive chunks of one lane, plus the scales and zero-points
 // of the batch's U * 128 / G groups for the wave's 16 rows, loaded with
@@ -119,6 +119,34 @@ __device__ __forceinline__ void load_batch(Batch<G, U> &b, const uint8_t *crow,
 __device__ __forceinline__ uint32_t batch_sz(const uint32_t *packed, int h, int lane) {
     const int src = ((lane & 15) * 4 + (h & 3)) * 4;     // byte address of the source lane
     return __builtin_amdgcn_ds_bpermute(src, packed[h >> 2]);
+}
+
+// The same batch through buffer loads: the addresses are a per-lane offset
+// that never changes (row lane % 16 of the tile, quarter lane / 16) plus a
+// wave-uniform part, so a load costs no vector arithmetic. The resource
+// covers the tile's valid rows only: reads past them (rows >= N) return 0.
+// Reads past the end of a row (the padded last chunk when K % 128 != 0, or
+// groups past K / G) land in the next row or return 0; they only meet x = 0
+// and xs = 0 and add nothing.
+template <int G, int U>
+__device__ __forceinline__ void load_batch_buf(Batch<G, U> &b, __amdgpu_buffer_rsrc_t crs,
+                                               __amdgpu_buffer_rsrc_t srs,
+                                               __amdgpu_buffer_rsrc_t zrs, int cvo, int svo,
+                                               int c, int c_last) {
+    constexpr int GPC = 128 / G;
+    constexpr int OOB = 0x40000000;             // past any resource: reads 0, no traffic
+#pragma unroll
+    for (int r = 0; r < Batch<G, U>::R; ++r) {
+        const int so = (c * GPC + 4 * r) * 2;
+        b.s[r] = __builtin_amdgcn_raw_buffer_load_b16(srs, svo, so, 0);
+        b.z[r] = __builtin_amdgcn_raw_buffer_load_b16(zrs, svo, so, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        // chunks past this wave's segment are never computed: not fetched
+        const int so = c + u <= c_last ? (c + u) * 64 : OOB;
+        b.q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo, so, 0);
+    }
 }
 
 template <int G, int NW>
@@ -249,75 +277,123 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
     }
 }
 
-// Persistent variant for M <= 4 and M * K small enough to keep x in LDS:
-// one block per compute unit stages x once (interleaved, zero padded to
-// whole chunks) together with the per-group sums xs[g][m] = sum_{k in g}
-// x[m][k], then streams 16-row tiles blockIdx.x, blockIdx.x + gridDim.x, ...
-// Each wave keeps the same run of K chunks for every tile, and the codes of
-// the next (tile, batch) are in flight while the current one is computed.
-// One barrier per tile combines the waves' partial sums (double-buffered).
-// Only lanes 0..15 (rows 0..3 of the MFMA output) carry live outputs.
-template <int G, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void gemv_stream_kernel(
+// Persistent split-K variant for M <= 4 with x[0:M, :] staged whole in LDS
+// (interleaved, zero padded to whole chunks) together with the per-group
+// sums xs[g][m] = sum_{k in g} x[m][k].
+//
+// The 8 waves of a block work on T = 8 / S tiles of 16 rows at a time; the
+// S waves of a tile split its K range (S = 1, 2, 4 or 8, chosen by the host
+// so that the grid has enough waves in flight: narrow layers split K more).
+// A wave streams its (tile, K segment) items with the codes of the next two
+// items in flight while the current one is computed. With S > 1 the partial
+// sums of a tile meet in LDS (one barrier per block step, double buffered);
+// with S = 1 each wave stores its tile directly. Only lanes 0..15 (rows 0..3
+// of the MFMA output) carry live outputs.
+template <int G, int S>
+__global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y) {
+    constexpr int NW = GV_SPLIT_WAVES;
+    constexpr int T = NW / S;                   // tiles per block step
     constexpr int SPG = G / 32;
     constexpr int GPC = 128 / G;
     constexpr int U = G == 32 ? 2 : 4;
     constexpr int LPG = G / 8;                  // staging lanes per group
-    // dynamic LDS: x [M][kr] bf16 | xs [kr/G][4] f32 | red [2][NW][4][16] f32
+    constexpr int MM = GV_SPLIT_MAX_M;
+    // dynamic LDS: x [M][kr] bf16 | xs [kr/G][MM] f32 | red [2][NW][MM][16] f32
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
     const int nl = lane & 15;
     const int kb = lane >> 4;
+    const int ts = wave / S, sg = wave % S;
     const int nchunk = (K + 127) >> 7;
     const int kr = nchunk * 128;                // LDS row length (zero padded)
     uint16_t *xl = reinterpret_cast<uint16_t *>(smem);
-    float(*xs)[GV_STREAM_MAX_M] = reinterpret_cast<float(*)[GV_STREAM_MAX_M]>(
-        smem + static_cast<size_t>(M) * kr * 2);
-    float(*red)[NW][GV_STREAM_MAX_M][16] = reinterpret_cast<float(*)[NW][GV_STREAM_MAX_M][16]>(
-        smem + static_cast<size_t>(M) * kr * 2 + static_cast<size_t>(kr / G) * GV_STREAM_MAX_M * 4);
+    float(*xs)[MM] = reinterpret_cast<float(*)[MM]>(smem + static_cast<size_t>(M) * kr * 2);
+    float(*red)[NW][MM][16] = reinterpret_cast<float(*)[NW][MM][16]>(
+        smem + static_cast<size_t>(M) * kr * 2 + static_cast<size_t>(kr / G) * MM * 4);
     const int ngroups = K / G;
     const int ntiles = (N + 15) >> 4;
-    const int my_tiles = (ntiles - static_cast<int>(blockIdx.x) + gridDim.x - 1) / gridDim.x;
+    const int nsteps = (ntiles + T - 1) / T;    // block steps in the grid
+    const int my_steps = (nsteps - static_cast<int>(blockIdx.x) + gridDim.x - 1) / gridDim.x;
     const int mrow = nl < M ? nl : M - 1;
     const Unpack128 uc = unpack128_consts();
 
-    const int cb = wave * nchunk / NW;
-    const int ce = (wave + 1) * nchunk / NW;
+    // this wave's K segment (whole chunks); every wave runs nb batches per
+    // step (the longest segment's count), shorter segments skip the rest
+    const int cb = sg * nchunk / S;
+    const int ce = (sg + 1) * nchunk / S;
     const int c_last = max(cb, ce - 1);
-    const int nb = ((nchunk + NW - 1) / NW + U - 1) / U;
-    const int nitems = my_tiles * nb;
+    const int nb = ((nchunk + S - 1) / S + U - 1) / U;
+    const int nitems = my_steps * nb;
 
+    auto tile_of = [&](int st, int slot) {
+        return (static_cast<int>(blockIdx.x) + st * static_cast<int>(gridDim.x)) * T + slot;
+    };
+    // Loads are unconditional: items past the end reload the last one; the
+    // last block step may hold fewer tiles, its extra slots repeat the last.
+    const int cvo = nl * (K >> 1) + kb * 16;                  // code byte offset
+    const int svo = ((lane >> 2) * ngroups + (lane & 3)) * 2;  // s / z byte offset
     auto load = [&](Batch<G, U> &b, int item) {
-        const int t = item / nb;
-        const int c = cb + (item - t * nb) * U;
-        const int tile = blockIdx.x + t * gridDim.x;
-        const int n = min(tile * 16 + nl, N - 1);
-        load_batch<G, U>(b, codes + static_cast<int64_t>(n) * (K >> 1), scales, zeros,
-                         tile * 16, N, K, ngroups, c, c_last, lane);
+        // items past the end (issued by the fixed-depth pipeline) get an
+        // empty resource: their loads return 0 without touching memory
+        const bool live = item < nitems;
+        item = min(item, nitems - 1);
+        const int st = item / nb;
+        const int c = cb + (item - st * nb) * U;
+        const int tile = min(tile_of(st, ts), ntiles - 1);
+        const int rows = live ? min(16, N - tile * 16) : 0;
+        const int64_t row0 = static_cast<int64_t>(tile) * 16;
+        const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(codes + row0 * (K >> 1)), 0, rows * (K >> 1), 0x00020000);
+        const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(scales + row0 * ngroups), 0, rows * ngroups * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(zeros + row0 * ngroups), 0, rows * ngroups * 2, 0x00020000);
+        load_batch_buf<G, U>(b, crs, srs, zrs, cvo, svo, c, c_last);
     };
 
-    // issue the first loads, then stage x and its group sums
-    Batch<G, U> b0, b1;
-    if (nitems > 0) load(b0, 0);
-    const int per_row = kr >> 3;                // 16-byte pieces per row
-    for (int e = threadIdx.x; e < M * per_row; e += NW * 64) {
-        // a group's LPG pieces are consecutive lanes (M * per_row and the
-        // stride are multiples of LPG), so they reduce with DPP moves
-        const int m = e / per_row;
-        const int kk = (e - m * per_row) * 8;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (kk < K)
-            v = *reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(m) * K + kk);
-        *reinterpret_cast<u32x4 *>(&xl[m * kr + kk]) = interleave8_bf16(v);
-        float sum = (bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y)) +
-                    (bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w));
-        sum = group_sum<LPG>(sum);
-        if (((e & (LPG - 1)) == 0)) xs[kk / G][m] = sum;
+    // the first two items are in flight while x is staged
+    Batch<G, U> b0, b1, b2;
+    load(b0, 0);
+    if (nitems > 1) load(b1, 1);                // (the first wait may then be stricter)
+    {
+        const int per_row = kr >> 3;            // 16-byte pieces per row
+        const int npieces = M * per_row;
+        constexpr int XP = GV_X_ELEMS / 8 / (NW * 64);
+        // all loads first; pieces past K (the zero padding) and past the
+        // last row are out of the resource: they read 0 and fetch nothing
+        const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(x), 0, M * K * 2, 0x00020000);
+        u32x4 xv[XP];
+#pragma unroll
+        for (int j = 0; j < XP; ++j) {
+            xv[j] = u32x4{0u, 0u, 0u, 0u};
+            if (j * NW * 64 >= npieces) break;  // uniform: rounds that hold no piece
+            const int e = static_cast<int>(threadIdx.x) + j * NW * 64;
+            const int m = e / per_row;
+            const int kk = (e - m * per_row) * 8;
+            const int off = (e < npieces && kk < K) ? (m * K + kk) * 2 : 0x40000000;
+            xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < XP; ++j) {
+            const int e = threadIdx.x + j * NW * 64;
+            if (e >= npieces) break;
+            // a group's LPG pieces are consecutive lanes (npieces and the
+            // stride are multiples of LPG), so they reduce with DPP moves
+            const int m = e / per_row;
+            const int kk = (e - m * per_row) * 8;
+            const u32x4 v = xv[j];
+            *reinterpret_cast<u32x4 *>(&xl[m * kr + kk]) = interleave8_bf16(v);
+            float sum = (bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y)) +
+                        (bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w));
+            sum = group_sum<LPG>(sum);
+            if ((e & (LPG - 1)) == 0) xs[kk / G][m] = sum;
+        }
     }
     __syncthreads();
 
@@ -325,8 +401,8 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_stream_kernel(
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     auto step = [&](Batch<G, U> &b, int item) {
-        const int t = item / nb;
-        const int bi = item - t * nb;
+        const int st = item / nb;
+        const int bi = item - st * nb;
         const int c = cb + bi * U;
         uint32_t packed[Batch<G, U>::R];
 #pragma unroll
@@ -347,8 +423,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_stream_kernel(
                 accg = mfma16x16x32(a, as_bf16x8(w[0], w[1], w[2], w[3]),
                                     first ? zero4 : accg);
                 if ((j % SPG) == SPG - 1) {
-                    const int h = u * GPC + j / SPG;
-                    const uint32_t szv = batch_sz(packed, h, lane);
+                    const uint32_t szv = batch_sz(packed, u * GPC + j / SPG, lane);
                     const float sv = bf16_lo(szv);
                     const float zz = fmaf(-128.0f, sv, bf16_hi(szv));
                     const f32x4 xg = *reinterpret_cast<const f32x4 *>(&xs[cc * GPC + j / SPG][0]);
@@ -362,23 +437,35 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_stream_kernel(
                 }
             }
         }
-        if (bi == nb - 1) {                     // end of tile t: combine waves
-            const int par = t & 1;
+        if (bi != nb - 1) return;               // end of this block step
+        if constexpr (S == 1) {
+            const int col = tile_of(st, ts) * 16 + nl;
+            if (kb == 0 && col < N) {
+                const float bv = bias ? bf16_to_f32(bias[col]) : 0.0f;
+#pragma unroll
+                for (int i = 0; i < MM; ++i)
+                    if (i < M)
+                        y[static_cast<int64_t>(i) * N + col] =
+                            static_cast<uint16_t>(f32_to_bf16_rne(acc[i] + bv));
+            }
+            acc = zero4;
+        } else {
+            const int par = st & 1;
             if (kb == 0) {
 #pragma unroll
-                for (int i = 0; i < GV_STREAM_MAX_M; ++i)
-                    if (i < M) red[par][wave][i][nl] = acc[i];
+                for (int i = 0; i < MM; ++i) red[par][wave][i][nl] = acc[i];
             }
             acc = zero4;
             __syncthreads();
-            const int tile = blockIdx.x + t * gridDim.x;
-            for (int e = threadIdx.x; e < M * 16; e += NW * 64) {
-                const int m = e >> 4;
-                const int nn = e & 15;
+            for (int e = threadIdx.x; e < T * M * 16; e += NW * 64) {
+                const int slot = e / (M * 16);
+                const int rem = e - slot * (M * 16);
+                const int m = rem >> 4;
+                const int nn = rem & 15;
                 float sum = 0.f;
 #pragma unroll
-                for (int w = 0; w < NW; ++w) sum += red[par][w][m][nn];
-                const int col = tile * 16 + nn;
+                for (int w = 0; w < S; ++w) sum += red[par][slot * S + w][m][nn];
+                const int col = tile_of(st, slot) * 16 + nn;
                 if (col < N) {
                     if (bias) sum += bf16_to_f32(bias[col]);
                     y[static_cast<int64_t>(m) * N + col] =
@@ -388,14 +475,15 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_stream_kernel(
         }
     };
 
-    int i = 0;
-    while (i < nitems) {
-        if (i + 1 < nitems) load(b1, i + 1);
+    for (int i = 0; i < nitems; i += 3) {
+        load(b2, i + 2);
         step(b0, i);
-        if (++i >= nitems) break;
-        if (i + 1 < nitems) load(b0, i + 1);
-        step(b1, i);
-        ++i;
+        if (i + 1 >= nitems) break;
+        load(b0, i + 3);
+        step(b1, i + 1);
+        if (i + 2 >= nitems) break;
+        load(b1, i + 4);
+        step(b2, i + 2);
     }
 }
 
@@ -413,35 +501,59 @@ int compute_units() {
     return cus[dev];
 }
 
-template <int G>
-hipError_t launch_stream(const uint16_t *x, int M, const uint8_t *codes,
-                         const uint16_t *scales, const uint16_t *zeros,
-                         const uint16_t *bias, int N, int K, uint16_t *y,
-                         hipStream_t stream) {
-    constexpr int NW = GV_STREAM_WAVES;
-    auto kern = gemv_stream_kernel<G, NW>;
+// Dynamic LDS of the split kernel for (M, K); 0 when x does not fit.
+size_t split_lds_bytes(int M, int K, int G) {
+    const size_t kr = static_cast<size_t>((K + 127) / 128) * 128;
+    return static_cast<size_t>(M) * kr * 2 + (kr / G) * GV_SPLIT_MAX_M * 4 +
+           2 * GV_SPLIT_WAVES * GV_SPLIT_MAX_M * 16 * 4;
+}
+
+template <int G, int S>
+hipError_t launch_split_s(const uint16_t *x, int M, const uint8_t *codes,
+                          const uint16_t *scales, const uint16_t *zeros,
+                          const uint16_t *bias, int N, int K, uint16_t *y,
+                          hipStream_t stream) {
+    auto kern = gemv_split_kernel<G, S>;
     static bool attr_set[64] = {false};         // per device
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
     if (dev < 0 || dev >= 64 || !attr_set[dev]) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 GV_STREAM_MAX_LDS);
+                                                 GV_SPLIT_MAX_LDS);
         if (e != hipSuccess) return e;
         if (dev >= 0 && dev < 64) attr_set[dev] = true;
     }
-    const int ntiles = (N + 15) / 16;
-    const int kr = (K + 127) / 128 * 128;
-    const size_t lds = static_cast<size_t>(M) * kr * 2 +
-                       static_cast<size_t>(kr / G) * GV_STREAM_MAX_M * 4 +
-                       2 * NW * GV_STREAM_MAX_M * 16 * 4;
-    // resident blocks per compute unit: LDS (160 KB) and 2 blocks of NW waves
+    const size_t lds = split_lds_bytes(M, K, G);
+    // resident blocks per compute unit: LDS (160 KB) and 2 blocks of 8 waves
     int per_cu = static_cast<int>((160 * 1024) / lds);
     per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
+    const int ntiles = (N + 15) / 16;
+    constexpr int T = GV_SPLIT_WAVES / S;
+    const int nsteps = (ntiles + T - 1) / T;
     const int slots = compute_units() * per_cu;
-    const int blocks = ntiles < slots ? ntiles : slots;
-    kern<<<dim3(blocks), dim3(NW * 64), lds, stream>>>(x, M, codes, scales, zeros, bias, N, K, y);
+    const int blocks = nsteps < slots ? nsteps : slots;
+    kern<<<dim3(blocks), dim3(GV_SPLIT_WAVES * 64), lds, stream>>>(x, M, codes, scales, zeros,
+                                                                   bias, N, K, y);
     return hipGetLastError();
+}
+
+// K split: 8 waves per tile (measured best for the decode layers: wide
+// layers keep 8-way splits too, the persistent grid streams their tiles),
+// fewer when K has fewer than 8 chunks.
+template <int G>
+hipError_t launch_split(const uint16_t *x, int M, const uint8_t *codes,
+                        const uint16_t *scales, const uint16_t *zeros,
+                        const uint16_t *bias, int N, int K, uint16_t *y,
+                        hipStream_t stream) {
+    const int nchunk = (K + 127) / 128;
+    if (nchunk >= 8)
+        return launch_split_s<G, 8>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+    if (nchunk >= 4)
+        return launch_split_s<G, 4>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+    if (nchunk >= 2)
+        return launch_split_s<G, 2>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+    return launch_split_s<G, 1>(x, M, codes, scales, zeros, bias, N, K, y, stream);
 }
 
 template <int G>
@@ -451,8 +563,8 @@ hipError_t launch_gemv_g(const uint16_t *x, int M, const uint8_t *codes,
                          hipStream_t stream) {
     const int ntiles = (N + 15) / 16;
     const int kr = (K + 127) / 128 * 128;
-    if (M <= GV_STREAM_MAX_M && static_cast<int64_t>(M) * kr <= GV_X_ELEMS) {
-        return launch_stream<G>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+    if (M <= GV_SPLIT_MAX_M && static_cast<int64_t>(M) * kr <= GV_X_ELEMS) {
+        return launch_split<G>(x, M, codes, scales, zeros, bias, N, K, y, stream);
     }
     gemv_phased_kernel<G, GV_WAVES><<<dim3(ntiles), dim3(GV_WAVES * 64), 0, stream>>>(
         x, M, codes, scales, zeros, bias, N, K, y);
