@@ -12,7 +12,7 @@
 // the flat array is (n, g) = (f / (K/G), f % (K/G)) and the scale/zero arrays
 // [N, K/G] are indexed by the flat group number; likewise codes are the flat
 // chunk number times 8 bytes. A group is G/16 consecutive lanes (2, 4 or 8,
-// aligned inside a DPP row), which reduce min/max with DPP moves.
+// aligned inside a DPP row), which reduce min/max with DPP ops.
 //
 // Exactness: the scale uses a correctly rounded binary32 divide (built with
 // correctly rounded division; no fp contraction in this file). Codes use
@@ -56,6 +56,25 @@ __device__ __forceinline__ float max3_abs2(float a, float b, float c) {
     return d;
 }
 
+// min / max of a and the same register of a partner lane, in one DPP op:
+// xor 1 / xor 2 inside each quad, or the mirror inside each half row. The
+// two wait states a DPP read needs after a VALU write of its source are
+// inside the asm.
+#define W4_DPP_MINMAX(name, op, ctrl)                                                   \
+    __device__ __forceinline__ float name(float a) {                                    \
+        float d;                                                                        \
+        asm("s_nop 1\n\t" op " %0, %1, %1 " ctrl " row_mask:0xf bank_mask:0xf"        \
+            : "=v"(d) : "v"(a));                                                        \
+        return d;                                                                       \
+    }
+W4_DPP_MINMAX(min_xor1, "v_min_f32_dpp", "quad_perm:[1,0,3,2]")
+W4_DPP_MINMAX(max_xor1, "v_max_f32_dpp", "quad_perm:[1,0,3,2]")
+W4_DPP_MINMAX(min_xor2, "v_min_f32_dpp", "quad_perm:[2,3,0,1]")
+W4_DPP_MINMAX(max_xor2, "v_max_f32_dpp", "quad_perm:[2,3,0,1]")
+W4_DPP_MINMAX(min_hmirror, "v_min_f32_dpp", "row_half_mirror")
+W4_DPP_MINMAX(max_hmirror, "v_max_f32_dpp", "row_half_mirror")
+#undef W4_DPP_MINMAX
+
 // One lane quantizes 16 consecutive elements (two 16-byte loads); a group is
 // G/16 consecutive lanes (2, 4 or 8 inside one DPP row).
 template <int G>
@@ -78,19 +97,19 @@ __device__ __forceinline__ void quantize16(const u32x4 d0, const u32x4 d1, int64
         mn = min3f(mn, v[i], v[i + 1]);
         mx = max3f(mx, v[i], v[i + 1]);
     }
-    mn = fminf(mn, v[15]);
-    mx = fmaxf(mx, v[15]);
+    mn = min3f(mn, v[15], v[15]);
+    mx = max3f(mx, v[15], v[15]);
     if constexpr (LPG >= 2) {
-        mn = fminf(mn, dpp_f32<DPP_QUAD_XOR1>(mn));
-        mx = fmaxf(mx, dpp_f32<DPP_QUAD_XOR1>(mx));
+        mn = min_xor1(mn);
+        mx = max_xor1(mx);
     }
     if constexpr (LPG >= 4) {
-        mn = fminf(mn, dpp_f32<DPP_QUAD_XOR2>(mn));
-        mx = fmaxf(mx, dpp_f32<DPP_QUAD_XOR2>(mx));
+        mn = min_xor2(mn);
+        mx = max_xor2(mx);
     }
     if constexpr (LPG >= 8) {
-        mn = fminf(mn, dpp_f32<DPP_ROW_HALF_MIRROR>(mn));
-        mx = fmaxf(mx, dpp_f32<DPP_ROW_HALF_MIRROR>(mx));
+        mn = min_hmirror(mn);
+        mx = max_hmirror(mx);
     }
     const float lo = mn + 0.0f;                // -0 -> +0
     const float hi = mx + 0.0f;
