@@ -154,12 +154,14 @@ __device__ __forceinline__ void quantize16(const u32x4 d0, const u32x4 d1, int64
         }
     }
     __builtin_nontemporal_store(u32x2{out0, out1}, codes + c);
-    // Every lane of the group stores the group's (identical) scale and
-    // zero-point: unconditional stores keep the number of outstanding memory
-    // operations fixed, so the loop waits only for the loads it needs.
-    const int64_t grp = c / LPG;
-    scales[grp] = static_cast<uint16_t>(sb);
-    zeros[grp] = static_cast<uint16_t>(zb);
+    // The first lane of each group stores the group's scale and zero-point
+    // (a lane mask, not a branch: every chunk issues the same stores, so the
+    // loop waits only for the loads it needs).
+    if ((c & (LPG - 1)) == 0) {
+        const int64_t grp = c / LPG;
+        scales[grp] = static_cast<uint16_t>(sb);
+        zeros[grp] = static_cast<uint16_t>(zb);
+    }
 }
 
 template <int G>
