@@ -179,7 +179,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "step", "gemv", "gemm", "quantize", "copy"],
+    ap.add_argument("--only", choices=["all", "step", "gemv", "gemv16", "gemm", "quantize", "copy"],
                     default="all", help="restrict to one part (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -328,6 +328,37 @@ def main():
             "set_back_to_back_GBps": round(tot_b / (set_ms * 1e-3) / 1e9, 1),
         }
         del gsets
+
+    # ---- small-batch decode GEMV, M = 16, G = 32 (same layer shapes) ------
+    if args.only in ("all", "gemv16"):
+        M16, G16 = 16, 32
+        gb16 = sum(linear_bytes(M16, N, K, G16) for N, K in layers.values())
+        n16 = max(2, -(-ROTATE_BYTES // gb16))
+        log(f"gemv M=16: {n16} rotating quantized copies of {gb16 / 1e6:.1f} MB")
+        per = {}
+        tot_ms = 0.0
+        tot_b = 0
+        for li, (name, (N, K)) in enumerate(layers.items()):
+            copies = []
+            for r in range(n16):
+                W, x = make_layer(torch, N, K, 7000 + 100 * r + li, M16, dev)
+                c, s_, z = w4.quantize_int4_grouped(W, G16)
+                del W
+                copies.append((x, c, s_, z, torch.empty((M16, N), dtype=torch.bfloat16, device=dev)))
+            fns = [(lambda e=e: w4.w4a16_linear(e[0], e[1], e[2], e[3], G16, out=e[4])) for e in copies]
+            g = graph_of(torch, fns)
+            ms = time_graphs(torch, [g], max(2, reps // 2)) / n16
+            b = linear_bytes(M16, N, K, G16)
+            per[name] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1)}
+            tot_ms += ms
+            tot_b += b
+            del g, copies, fns
+        out["gemv_m16_g32"] = {
+            "kernel": "gemv_phased_kernel<32, 8>", "bound": "hbm",
+            "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
+            "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_set": tot_b, "per_layer": per,
+        }
 
     # ---- prefill GEMM, Gemma3-12B-shaped layers, M = 2048 ----------------
     if args.only in ("all", "gemm"):

@@ -237,13 +237,33 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
         if (k_phase > 0) __syncthreads();        // previous phase fully consumed
         const int kw = min(kp, ((K - k_phase + 127) >> 7) << 7);
         const int per_row = kw >> 3;            // 16-byte pieces per row
-        for (int e = threadIdx.x; e < M * per_row; e += NW * 64) {
-            const int m = e / per_row;
-            const int kk = (e - m * per_row) * 8;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (k_phase + kk < K)
-                v = *reinterpret_cast<const u32x4 *>(x + static_cast<int64_t>(m) * K + k_phase + kk);
-            *reinterpret_cast<u32x4 *>(&xl[m * kp + kk]) = interleave8_bf16(v);
+        const int npieces = M * per_row;        // at most GV_X_ELEMS / 8
+        {
+            // all of a thread's pieces are loaded first (pieces past K read 0
+            // from outside the resource), then interleaved into LDS
+            constexpr int XP = GV_X_ELEMS / 8 / (NW * 64);
+            const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t *>(x), 0, M * K * 2, 0x00020000);
+            u32x4 xv[XP];
+#pragma unroll
+            for (int j = 0; j < XP; ++j) {
+                xv[j] = u32x4{0u, 0u, 0u, 0u};
+                if (j * NW * 64 >= npieces) break;  // uniform
+                const int e = static_cast<int>(threadIdx.x) + j * NW * 64;
+                const int m = e / per_row;
+                const int kk = (e - m * per_row) * 8;
+                const int off = (e < npieces && k_phase + kk < K) ? (m * K + k_phase + kk) * 2
+                                                                  : 0x40000000;
+                xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < XP; ++j) {
+                const int e = static_cast<int>(threadIdx.x) + j * NW * 64;
+                if (e >= npieces) break;
+                const int m = e / per_row;
+                const int kk = (e - m * per_row) * 8;
+                *reinterpret_cast<u32x4 *>(&xl[m * kp + kk]) = interleave8_bf16(xv[j]);
+            }
         }
         __syncthreads();
 
