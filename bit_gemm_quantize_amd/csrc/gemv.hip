@@ -297,9 +297,10 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
     }
 }
 
-// Persistent split-K variant for M <= 4 with x[0:M, :] staged whole in LDS
+// Persistent split-K variant for M <= 4 with x[0:M, :] staged in LDS
 // (interleaved, zero padded to whole chunks) together with the per-group
-// sums xs[g][m] = sum_{k in g} x[m][k].
+// sums xs[g][m] = sum_{k in g} x[m][k]; each wave stages the K segment it
+// reads.
 //
 // The 8 waves of a block work on T = 8 / S tiles of 16 rows at a time; the
 // S waves of a tile split its K range (S = 1, 2, 4 or 8, chosen by the host
@@ -376,46 +377,83 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
         load_batch_buf<G, U>(b, crs, srs, zrs, cvo, svo, c, c_last);
     };
 
-    // the first two items are in flight while x is staged
+    // x staging, per wave: a wave stages only the K segment it reads (rows
+    // 0..M-1, whole chunks), so no block barrier is needed before the first
+    // step; waves that share a segment (T > 1) write identical values. When
+    // the segment takes one round of loads (M * pieces <= 4 * 64), that round
+    // is issued ahead of the codes of the first two items, so the wait for x
+    // leaves the codes in flight; larger segments go row by row beforehand.
     Batch<G, U> b0, b1, b2;
-    load(b0, 0);
-    if (nitems > 1) load(b1, 1);                // (the first wait may then be stricter)
     {
-        const int per_row = kr >> 3;            // 16-byte pieces per row
-        const int npieces = M * per_row;
-        constexpr int XP = GV_X_ELEMS / 8 / (NW * 64);
-        // all loads first; pieces past K (the zero padding) and past the
-        // last row are out of the resource: they read 0 and fetch nothing
+        constexpr int XW = 4;                   // 16-byte pieces per lane per round
+        const int seg_pr = (ce - cb) * 16;      // pieces per row of the segment
+        const int k0 = cb * 128;
+        const bool one_round = M * seg_pr <= XW * 64;
+        const int rpr = (seg_pr + XW * 64 - 1) / (XW * 64);   // rounds per row
+        const int nrounds = one_round ? 1 : M * rpr;
         const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(x), 0, M * K * 2, 0x00020000);
-        u32x4 xv[XP];
+        u32x4 xv[XW];
+        // round r covers pieces e = e0 + j * 64 + lane (e0 = 0 in the single
+        // round, which spans all rows; else row r / rpr from its (r % rpr)-th
+        // run); pieces past the segment or past K are out of the resource:
+        // they read 0 and fetch nothing
+        auto piece = [&](int r, int j, int &m, int &p) {
+            if (one_round) {
+                // e / seg_pr without a divide: one_round implies e < 4 * seg_pr
+                // for every live piece (M <= 4)
+                const int e = j * 64 + lane;
+                m = (e >= seg_pr) + (e >= 2 * seg_pr) + (e >= 3 * seg_pr) + (e >= 4 * seg_pr);
+                p = e - m * seg_pr;
+            } else {
+                m = r / rpr;
+                p = (r - m * rpr) * (XW * 64) + j * 64 + lane;
+            }
+        };
+        auto issue = [&](int r) {
 #pragma unroll
-        for (int j = 0; j < XP; ++j) {
-            xv[j] = u32x4{0u, 0u, 0u, 0u};
-            if (j * NW * 64 >= npieces) break;  // uniform: rounds that hold no piece
-            const int e = static_cast<int>(threadIdx.x) + j * NW * 64;
-            const int m = e / per_row;
-            const int kk = (e - m * per_row) * 8;
-            const int off = (e < npieces && kk < K) ? (m * K + kk) * 2 : 0x40000000;
-            xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
-        }
+            for (int j = 0; j < XW; ++j) {
+                int m, p;
+                piece(r, j, m, p);
+                const int kk = k0 + p * 8;
+                const int off = (m < M && p < seg_pr && kk < K) ? (m * K + kk) * 2 : 0x40000000;
+                xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+            }
+        };
+        const int round_pieces = one_round ? M * seg_pr : seg_pr;
+        auto put = [&](int r) {
 #pragma unroll
-        for (int j = 0; j < XP; ++j) {
-            const int e = threadIdx.x + j * NW * 64;
-            if (e >= npieces) break;
-            // a group's LPG pieces are consecutive lanes (npieces and the
-            // stride are multiples of LPG), so they reduce with DPP moves
-            const int m = e / per_row;
-            const int kk = (e - m * per_row) * 8;
-            const u32x4 v = xv[j];
-            *reinterpret_cast<u32x4 *>(&xl[m * kr + kk]) = interleave8_bf16(v);
-            float sum = (bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y)) +
-                        (bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w));
-            sum = group_sum<LPG>(sum);
-            if ((e & (LPG - 1)) == 0) xs[kk / G][m] = sum;
+            for (int j = 0; j < XW; ++j) {
+                const int jb = one_round ? j * 64 : (r % rpr) * (XW * 64) + j * 64;
+                if (jb >= round_pieces) break;  // uniform
+                int m, p;
+                piece(r, j, m, p);
+                const bool ok = m < M && p < seg_pr;
+                const int kk = k0 + p * 8;
+                const u32x4 v = xv[j];
+                if (ok) *reinterpret_cast<u32x4 *>(&xl[m * kr + kk]) = interleave8_bf16(v);
+                float sum = (bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y)) +
+                            (bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w));
+                // a group's LPG pieces sit in consecutive lanes (LPG divides
+                // 16, hence seg_pr and 64), so they reduce with DPP moves
+                sum = group_sum<LPG>(sum);
+                if (ok && (lane & (LPG - 1)) == 0) xs[kk / G][m] = sum;
+            }
+        };
+        if (one_round) {
+            issue(0);
+        } else {
+            for (int r = 0; r < nrounds; ++r) {
+                issue(r);
+                put(r);
+            }
         }
+        // items past the end get an empty resource (nitems >= 1 always)
+        load(b0, 0);
+        load(b1, 1);
+        if (one_round) put(0);
+        __builtin_amdgcn_wave_barrier();
     }
-    __syncthreads();
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
