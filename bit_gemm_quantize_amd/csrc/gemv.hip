@@ -70,10 +70,9 @@ __device__ __forceinline__ void align_groups(u32x4 &d) {
 
 constexpr int GV_WAVES = 8;              // waves per block (split of K)
 constexpr int GV_X_ELEMS = 32768;        // bf16 elements of x staged in LDS
-constexpr int GV_SPLIT_MAX_M = 4;       // split-K kernel: M <= 4
+constexpr int GV_SPLIT_MAX_M = 16;      // split-K kernel: M <= 16 ...
 constexpr int GV_SPLIT_WAVES = 8;       // split-K kernel: waves per block
-constexpr int GV_SPLIT_MAX_LDS = GV_X_ELEMS * 2 + (GV_X_ELEMS / 32) * GV_SPLIT_MAX_M * 4 +
-                                 2 * GV_SPLIT_WAVES * GV_SPLIT_MAX_M * 16 * 4;
+constexpr int GV_SPLIT_MAX_LDS = 160 * 1024;   // ... when its LDS fits one CU
 
 // Codes of U consecutive chunks of one lane, plus the scales and zero-points
 // of the batch's U * 128 / G groups for the wave's 16 rows, loaded with
@@ -297,10 +296,10 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
     }
 }
 
-// Persistent split-K variant for M <= 4 with x[0:M, :] staged in LDS
-// (interleaved, zero padded to whole chunks) together with the per-group
-// sums xs[g][m] = sum_{k in g} x[m][k]; each wave stages the K segment it
-// reads.
+// Persistent split-K kernel for 1 <= M <= 16 when x fits in LDS: x[0:M, :]
+// is staged in LDS (interleaved, zero padded to whole chunks) together with
+// the per-group sums xs[g][m] = sum_{k in g} x[m][k]; each wave stages the K
+// segment it reads.
 //
 // The 8 waves of a block work on T = 8 / S tiles of 16 rows at a time; the
 // S waves of a tile split its K range (S = 1, 2, 4 or 8, chosen by the host
@@ -308,8 +307,9 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
 // A wave streams its (tile, K segment) items with the codes of the next two
 // items in flight while the current one is computed. With S > 1 the partial
 // sums of a tile meet in LDS (one barrier per block step, double buffered);
-// with S = 1 each wave stores its tile directly. Only lanes 0..15 (rows 0..3
-// of the MFMA output) carry live outputs.
+// with S = 1 each wave stores its tile directly. Lane (nl, kb) holds output
+// rows 4 kb .. 4 kb + 3 of column nl; rows >= M are computed (their A rows
+// repeat row M - 1) and never stored.
 template <int G, int S>
 __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
@@ -321,8 +321,7 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
     constexpr int GPC = 128 / G;
     constexpr int U = G == 32 ? 2 : 4;
     constexpr int LPG = G / 8;                  // staging lanes per group
-    constexpr int MM = GV_SPLIT_MAX_M;
-    // dynamic LDS: x [M][kr] bf16 | xs [kr/G][MM] f32 | red [2][NW][MM][16] f32
+    // dynamic LDS: x [M][kr] bf16 | xs [kr/G][mr] f32 | red [2][NW][mr][16] f32
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int lane = threadIdx.x & 63;
@@ -332,15 +331,16 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
     const int ts = wave / S, sg = wave % S;
     const int nchunk = (K + 127) >> 7;
     const int kr = nchunk * 128;                // LDS row length (zero padded)
+    const int mr = (M + 3) & ~3;                // rows of xs and red
     uint16_t *xl = reinterpret_cast<uint16_t *>(smem);
-    float(*xs)[MM] = reinterpret_cast<float(*)[MM]>(smem + static_cast<size_t>(M) * kr * 2);
-    float(*red)[NW][MM][16] = reinterpret_cast<float(*)[NW][MM][16]>(
-        smem + static_cast<size_t>(M) * kr * 2 + static_cast<size_t>(kr / G) * MM * 4);
+    float *xs = reinterpret_cast<float *>(smem + static_cast<size_t>(M) * kr * 2);
+    float *red = xs + static_cast<size_t>(kr / G) * mr;
     const int ngroups = K / G;
     const int ntiles = (N + 15) >> 4;
     const int nsteps = (ntiles + T - 1) / T;    // block steps in the grid
     const int my_steps = (nsteps - static_cast<int>(blockIdx.x) + gridDim.x - 1) / gridDim.x;
     const int mrow = nl < M ? nl : M - 1;
+    const int kq = min(kb, (M - 1) >> 2);       // xs rows read by this lane (>= M: dead)
     const Unpack128 uc = unpack128_consts();
 
     // this wave's K segment (whole chunks); every wave runs nb batches per
@@ -379,79 +379,64 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
 
     // x staging, per wave: a wave stages only the K segment it reads (rows
     // 0..M-1, whole chunks), so no block barrier is needed before the first
-    // step; waves that share a segment (T > 1) write identical values. When
-    // the segment takes one round of loads (M * pieces <= 4 * 64), that round
-    // is issued ahead of the codes of the first two items, so the wait for x
-    // leaves the codes in flight; larger segments go row by row beforehand.
+    // step; waves that share a segment (T > 1) write identical values. The
+    // segment is cut in runs of 64 pieces of 16 bytes (one per lane) along
+    // each row; the first XR runs are issued ahead of the codes of the first
+    // two items, so the wait for x leaves the codes in flight.
     Batch<G, U> b0, b1, b2;
     {
-        constexpr int XW = 4;                   // 16-byte pieces per lane per round
+        constexpr int XR = 16;                  // runs per round
         const int seg_pr = (ce - cb) * 16;      // pieces per row of the segment
+        const int rpr = (seg_pr + 63) >> 6;     // runs per row
+        const int nruns = M * rpr;
         const int k0 = cb * 128;
-        const bool one_round = M * seg_pr <= XW * 64;
-        const int rpr = (seg_pr + XW * 64 - 1) / (XW * 64);   // rounds per row
-        const int nrounds = one_round ? 1 : M * rpr;
         const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(x), 0, M * K * 2, 0x00020000);
-        u32x4 xv[XW];
-        // round r covers pieces e = e0 + j * 64 + lane (e0 = 0 in the single
-        // round, which spans all rows; else row r / rpr from its (r % rpr)-th
-        // run); pieces past the segment or past K are out of the resource:
-        // they read 0 and fetch nothing
-        auto piece = [&](int r, int j, int &m, int &p) {
-            if (one_round) {
-                // e / seg_pr without a divide: one_round implies e < 4 * seg_pr
-                // for every live piece (M <= 4)
-                const int e = j * 64 + lane;
-                m = (e >= seg_pr) + (e >= 2 * seg_pr) + (e >= 3 * seg_pr) + (e >= 4 * seg_pr);
-                p = e - m * seg_pr;
-            } else {
-                m = r / rpr;
-                p = (r - m * rpr) * (XW * 64) + j * 64 + lane;
-            }
-        };
-        auto issue = [&](int r) {
+        u32x4 xv[XR];
+        // run i covers row i / rpr, pieces 64 (i % rpr) + lane; pieces past
+        // the segment or past K are out of the resource: they read 0 and
+        // fetch nothing
+        auto issue = [&](int r0) {
+            int m = r0 / rpr, q = r0 - m * rpr;
 #pragma unroll
-            for (int j = 0; j < XW; ++j) {
-                int m, p;
-                piece(r, j, m, p);
+            for (int j = 0; j < XR; ++j) {
+                if (r0 + j >= nruns) break;     // uniform
+                const int p = q * 64 + lane;
                 const int kk = k0 + p * 8;
-                const int off = (m < M && p < seg_pr && kk < K) ? (m * K + kk) * 2 : 0x40000000;
+                const int off = (p < seg_pr && kk < K) ? (m * K + kk) * 2 : 0x40000000;
                 xv[j] = __builtin_amdgcn_raw_buffer_load_b128(xrs, off, 0, 0);
+                if (++q == rpr) { q = 0; ++m; }
             }
         };
-        const int round_pieces = one_round ? M * seg_pr : seg_pr;
-        auto put = [&](int r) {
+        auto put = [&](int r0) {
+            int m = r0 / rpr, q = r0 - m * rpr;
 #pragma unroll
-            for (int j = 0; j < XW; ++j) {
-                const int jb = one_round ? j * 64 : (r % rpr) * (XW * 64) + j * 64;
-                if (jb >= round_pieces) break;  // uniform
-                int m, p;
-                piece(r, j, m, p);
-                const bool ok = m < M && p < seg_pr;
+            for (int j = 0; j < XR; ++j) {
+                if (r0 + j >= nruns) break;     // uniform
+                const int p = q * 64 + lane;
                 const int kk = k0 + p * 8;
+                const bool ok = p < seg_pr;
                 const u32x4 v = xv[j];
                 if (ok) *reinterpret_cast<u32x4 *>(&xl[m * kr + kk]) = interleave8_bf16(v);
                 float sum = (bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y)) +
                             (bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w));
-                // a group's LPG pieces sit in consecutive lanes (LPG divides
-                // 16, hence seg_pr and 64), so they reduce with DPP moves
+                // a group's LPG pieces sit in consecutive lanes of one run
+                // (LPG divides 16, runs start at multiples of 512 k), so
+                // they reduce with DPP moves
                 sum = group_sum<LPG>(sum);
-                if (ok && (lane & (LPG - 1)) == 0) xs[kk / G][m] = sum;
+                if (ok && (lane & (LPG - 1)) == 0) xs[(kk / G) * mr + m] = sum;
+                if (++q == rpr) { q = 0; ++m; }
             }
         };
-        if (one_round) {
-            issue(0);
-        } else {
-            for (int r = 0; r < nrounds; ++r) {
-                issue(r);
-                put(r);
-            }
-        }
+        issue(0);
         // items past the end get an empty resource (nitems >= 1 always)
         load(b0, 0);
         load(b1, 1);
-        if (one_round) put(0);
+        put(0);
+        for (int r0 = XR; r0 < nruns; r0 += XR) {
+            issue(r0);
+            put(r0);
+        }
         __builtin_amdgcn_wave_barrier();
     }
 
@@ -484,7 +469,8 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
                     const uint32_t szv = batch_sz(packed, u * GPC + j / SPG, lane);
                     const float sv = bf16_lo(szv);
                     const float zz = fmaf(-128.0f, sv, bf16_hi(szv));
-                    const f32x4 xg = *reinterpret_cast<const f32x4 *>(&xs[cc * GPC + j / SPG][0]);
+                    const f32x4 xg = *reinterpret_cast<const f32x4 *>(
+                        &xs[(cc * GPC + j / SPG) * mr + 4 * kq]);
                     // All four MFMA results are consumed (also for M = 1):
                     // leaving some of them dead lets the register allocator
                     // reuse an MFMA destination register while the MFMA is
@@ -498,21 +484,21 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
         if (bi != nb - 1) return;               // end of this block step
         if constexpr (S == 1) {
             const int col = tile_of(st, ts) * 16 + nl;
-            if (kb == 0 && col < N) {
+            if (col < N) {
                 const float bv = bias ? bf16_to_f32(bias[col]) : 0.0f;
 #pragma unroll
-                for (int i = 0; i < MM; ++i)
-                    if (i < M)
-                        y[static_cast<int64_t>(i) * N + col] =
+                for (int i = 0; i < 4; ++i)
+                    if (4 * kb + i < M)
+                        y[static_cast<int64_t>(4 * kb + i) * N + col] =
                             static_cast<uint16_t>(f32_to_bf16_rne(acc[i] + bv));
             }
             acc = zero4;
         } else {
             const int par = st & 1;
-            if (kb == 0) {
+            float *rw = red + (static_cast<size_t>(par * NW + wave) * mr) * 16;
 #pragma unroll
-                for (int i = 0; i < MM; ++i) red[par][wave][i][nl] = acc[i];
-            }
+            for (int i = 0; i < 4; ++i)
+                if (4 * kb + i < M) rw[(4 * kb + i) * 16 + nl] = acc[i];
             acc = zero4;
             __syncthreads();
             for (int e = threadIdx.x; e < T * M * 16; e += NW * 64) {
@@ -520,9 +506,10 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
                 const int rem = e - slot * (M * 16);
                 const int m = rem >> 4;
                 const int nn = rem & 15;
+                const float *rp = red + (static_cast<size_t>(par * NW + slot * S) * mr + m) * 16 + nn;
                 float sum = 0.f;
 #pragma unroll
-                for (int w = 0; w < S; ++w) sum += red[par][slot * S + w][m][nn];
+                for (int w = 0; w < S; ++w) sum += rp[w * mr * 16];
                 const int col = tile_of(st, slot) * 16 + nn;
                 if (col < N) {
                     if (bias) sum += bf16_to_f32(bias[col]);
@@ -559,11 +546,26 @@ int compute_units() {
     return cus[dev];
 }
 
-// Dynamic LDS of the split kernel for (M, K); 0 when x does not fit.
+// LDS a workgroup may use on the current device (160 KB on gfx950).
+size_t max_lds_per_block() {
+    static size_t lds[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 64 * 1024;
+    if (lds[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            v <= 0)
+            v = 64 * 1024;
+        lds[dev] = static_cast<size_t>(v < GV_SPLIT_MAX_LDS ? v : GV_SPLIT_MAX_LDS);
+    }
+    return lds[dev];
+}
+
+// Dynamic LDS of the split kernel for (M, K).
 size_t split_lds_bytes(int M, int K, int G) {
     const size_t kr = static_cast<size_t>((K + 127) / 128) * 128;
-    return static_cast<size_t>(M) * kr * 2 + (kr / G) * GV_SPLIT_MAX_M * 4 +
-           2 * GV_SPLIT_WAVES * GV_SPLIT_MAX_M * 16 * 4;
+    const size_t mr = static_cast<size_t>((M + 3) & ~3);
+    return static_cast<size_t>(M) * kr * 2 + (kr / G) * mr * 4 + 2 * GV_SPLIT_WAVES * mr * 16 * 4;
 }
 
 template <int G, int S>
@@ -578,13 +580,13 @@ hipError_t launch_split_s(const uint16_t *x, int M, const uint8_t *codes,
     if (dev < 0 || dev >= 64 || !attr_set[dev]) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 GV_SPLIT_MAX_LDS);
+                                                 static_cast<int>(max_lds_per_block()));
         if (e != hipSuccess) return e;
         if (dev >= 0 && dev < 64) attr_set[dev] = true;
     }
     const size_t lds = split_lds_bytes(M, K, G);
     // resident blocks per compute unit: LDS (160 KB) and 2 blocks of 8 waves
-    int per_cu = static_cast<int>((160 * 1024) / lds);
+    int per_cu = static_cast<int>(static_cast<size_t>(GV_SPLIT_MAX_LDS) / lds);
     per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
     const int ntiles = (N + 15) / 16;
     constexpr int T = GV_SPLIT_WAVES / S;
@@ -620,8 +622,7 @@ hipError_t launch_gemv_g(const uint16_t *x, int M, const uint8_t *codes,
                          const uint16_t *bias, int N, int K, uint16_t *y,
                          hipStream_t stream) {
     const int ntiles = (N + 15) / 16;
-    const int kr = (K + 127) / 128 * 128;
-    if (M <= GV_SPLIT_MAX_M && static_cast<int64_t>(M) * kr <= GV_X_ELEMS) {
+    if (M <= GV_SPLIT_MAX_M && split_lds_bytes(M, K, G) <= max_lds_per_block()) {
         return launch_split<G>(x, M, codes, scales, zeros, bias, N, K, y, stream);
     }
     gemv_phased_kernel<G, GV_WAVES><<<dim3(ntiles), dim3(GV_WAVES * 64), 0, stream>>>(

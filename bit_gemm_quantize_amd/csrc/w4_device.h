@@ -79,12 +79,12 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 // ----------------------------------------------------------- code unpack
-// (a & mask) | c in one VALU op. gfx9 VOP3 takes no literal operands and at
-// most one scalar operand, so the mask comes in an SGPR and c in a VGPR.
+// (a & mask) | c: the compiler selects one v_and_or_b32 for it. It must
+// stay plain code: a VALU op written as inline asm is invisible to the
+// compiler's hazard checks, and placed next to a matrix-core op that reads
+// or writes the same registers it gave wrong, run-to-run varying results.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c) {
-    uint32_t d;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(c));
-    return d;
+    return (a & mask) | c;
 }
 
 // Constants of the nibble expansion, materialised once per kernel.
