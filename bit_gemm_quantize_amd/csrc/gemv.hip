@@ -70,6 +70,10 @@ __device__ __forceinline__ void align_groups(u32x4 &d) {
 
 constexpr int GV_WAVES = 8;              // waves per block (split of K)
 constexpr int GV_X_ELEMS = 32768;        // bf16 elements of x staged in LDS
+// Padding (bf16 elements) after each staged x row: an A-fragment read has
+// 16 lanes on 16 rows at one column; with rows 16 bytes apart modulo the
+// 256-byte bank period they fall in different banks instead of one.
+constexpr int GV_X_PAD = 8;
 constexpr int GV_SPLIT_MAX_M = 16;      // split-K kernel: M <= 16 ...
 constexpr int GV_SPLIT_WAVES = 8;       // split-K kernel: waves per block
 constexpr int GV_SPLIT_MAX_LDS = 160 * 1024;   // ... when its LDS fits one CU
@@ -80,8 +84,8 @@ constexpr int GV_SPLIT_MAX_LDS = 160 * 1024;   // ... when its LDS fits one CU
 // (s | z << 16) of row l / 4, group 4r + l % 4 of the batch.
 template <int G, int U>
 struct Batch {
-    static constexpr int GPB = U * 128 / G;     // groups per batch (4 or 8)
-    static constexpr int R = GPB / 4;
+    static constexpr int GPB = U * 128 / G;     // groups per batch (2, 4 or 8)
+    static constexpr int R = (GPB + 3) / 4;     // (GPB = 2: lanes l % 4 >= 2 unused)
     u32x4 q[U];
     uint32_t s[R];
     uint32_t z[R];
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
     constexpr int SPG = G / 32;                 // slots per group: 4, 2 or 1
     constexpr int GPC = 128 / G;                // groups per chunk: 1, 2 or 4
     constexpr int U = G == 32 ? 2 : 4;          // chunks per batch
-    __shared__ __attribute__((aligned(16))) uint16_t xl[GV_X_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t xl[GV_X_ELEMS + 16 * GV_X_PAD];
     __shared__ float red[NW][16][17];
 
     const int lane = threadIdx.x & 63;
@@ -178,6 +182,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
     // meet x = 0 and contribute nothing.
     const int kp = min(nchunk * 128, (GV_X_ELEMS / M) & ~127);
     const int cpp = kp >> 7;                    // chunks per phase
+    const int kps = kp + GV_X_PAD;              // LDS row stride
 
     // Loads are unconditional (clamped addresses), so the compiler can count
     // the loads in flight and wait only for the batch being computed.
@@ -203,7 +208,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
             for (int j = 0; j < 4; ++j) {
                 const bool first = (j % SPG) == 0;
                 const int ka = cc * 128 + slot_koff<G>(j, kb) - k_phase;
-                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(&xl[mrow * kp + ka]));
+                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(&xl[mrow * kps + ka]));
                 uint32_t w[4];
                 unpack8_bias128_il(b.q[u][j], w, uc);
                 xsg = mfma16x16x32(a, ones, first ? zero4 : xsg);
@@ -261,7 +266,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
                 if (e >= npieces) break;
                 const int m = e / per_row;
                 const int kk = (e - m * per_row) * 8;
-                *reinterpret_cast<u32x4 *>(&xl[m * kp + kk]) = interleave8_bf16(xv[j]);
+                *reinterpret_cast<u32x4 *>(&xl[m * kps + kk]) = interleave8_bf16(xv[j]);
             }
         }
         __syncthreads();
@@ -297,9 +302,17 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
 }
 
 // Persistent split-K kernel for 1 <= M <= 16 when x fits in LDS: x[0:M, :]
-// is staged in LDS (interleaved, zero padded to whole chunks) together with
-// the per-group sums xs[g][m] = sum_{k in g} x[m][k]; each wave stages the K
-// segment it reads.
+// is staged in LDS (zero padded to whole chunks) together with the
+// per-group sums xs[g][m] = sum_{k in g} x[m][k]; each wave stages the K
+// segment it reads. Two staging forms:
+//   NAT = false (small M): through registers, 8 values per 16 bytes put in
+//     the interleaved order of the 7-op code expansion, group sums from the
+//     loaded values, rows padded by 16 bytes against bank conflicts;
+//   NAT = true (larger M, where that staging costs more than it saves):
+//     global -> LDS copies with no register round trip, natural order (9-op
+//     expansion), 16-byte pieces of row m stored at piece ^ (m % 16) inside
+//     each 256-byte chunk so that the 16 rows of a fragment read fall in
+//     different banks, group sums by matrix-core products with ones.
 //
 // The 8 waves of a block work on T = 8 / S tiles of 16 rows at a time; the
 // S waves of a tile split its K range (S = 1, 2, 4 or 8, chosen by the host
@@ -310,7 +323,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
 // with S = 1 each wave stores its tile directly. Lane (nl, kb) holds output
 // rows 4 kb .. 4 kb + 3 of column nl; rows >= M are computed (their A rows
 // repeat row M - 1) and never stored.
-template <int G, int S>
+template <int G, int S, bool NAT>
 __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -321,7 +334,9 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
     constexpr int GPC = 128 / G;
     constexpr int U = G == 32 ? 2 : 4;
     constexpr int LPG = G / 8;                  // staging lanes per group
-    // dynamic LDS: x [M][kr] bf16 | xs [kr/G][mr] f32 | red [2][NW][mr][16] f32
+    constexpr int R = Batch<G, U>::R;
+    constexpr int MR = GV_SPLIT_MAX_M;          // rows of xs and red
+    // dynamic LDS: x [M][kr + pad] bf16 | xs [kr/G][MR] f32 | red [2][NW][MR][16] f32
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
     const int lane = threadIdx.x & 63;
@@ -330,11 +345,11 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
     const int kb = lane >> 4;
     const int ts = wave / S, sg = wave % S;
     const int nchunk = (K + 127) >> 7;
-    const int kr = nchunk * 128;                // LDS row length (zero padded)
-    const int mr = (M + 3) & ~3;                // rows of xs and red
+    const int kr = nchunk * 128;                // x row length (zero padded)
+    const int krs = NAT ? kr : kr + GV_X_PAD;   // LDS row stride
     uint16_t *xl = reinterpret_cast<uint16_t *>(smem);
-    float *xs = reinterpret_cast<float *>(smem + static_cast<size_t>(M) * kr * 2);
-    float *red = xs + static_cast<size_t>(kr / G) * mr;
+    float *xs = reinterpret_cast<float *>(smem + static_cast<size_t>(M) * krs * 2);
+    float *red = xs + static_cast<size_t>(kr / G) * MR;
     const int ngroups = K / G;
     const int ntiles = (N + 15) >> 4;
     const int nsteps = (ntiles + T - 1) / T;    // block steps in the grid
@@ -349,25 +364,29 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
     const int ce = (sg + 1) * nchunk / S;
     const int c_last = max(cb, ce - 1);
     const int nb = ((nchunk + S - 1) / S + U - 1) / U;
-    const int nitems = my_steps * nb;
 
-    auto tile_of = [&](int st, int slot) {
-        return (static_cast<int>(blockIdx.x) + st * static_cast<int>(gridDim.x)) * T + slot;
-    };
-    // Loads are unconditional: items past the end reload the last one; the
-    // last block step may hold fewer tiles, its extra slots repeat the last.
+    // Per-lane operand addresses; a chunk adds a wave-uniform offset and a
+    // slot j a constant one. slot_koff(j, kb) - slot_koff(0, kb) does not
+    // depend on kb.
+    const uint16_t *xa = &xl[mrow * krs + slot_koff<G>(0, kb)];
+    // NAT: byte offset of the lane's fragment j in chunk 0 (swizzled piece)
+    uint32_t xo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        xo[j] = (mrow * krs + ((slot_koff<G>(j, kb) >> 3) ^ (mrow & 15)) * 8) * 2;
+    const float *xsa = xs + 4 * kq;
     const int cvo = nl * (K >> 1) + kb * 16;                  // code byte offset
     const int svo = ((lane >> 2) * ngroups + (lane & 3)) * 2;  // s / z byte offset
-    auto load = [&](Batch<G, U> &b, int item) {
-        // items past the end (issued by the fixed-depth pipeline) get an
-        // empty resource: their loads return 0 without touching memory
-        const bool live = item < nitems;
-        item = min(item, nitems - 1);
-        const int st = item / nb;
-        const int c = cb + (item - st * nb) * U;
-        const int tile = min(tile_of(st, ts), ntiles - 1);
-        const int rows = live ? min(16, N - tile * 16) : 0;
-        const int64_t row0 = static_cast<int64_t>(tile) * 16;
+
+    // Items are loaded and computed in order: (block step st, batch bi).
+    // Items past the end (issued by the fixed-depth pipeline) and tiles past
+    // N get an empty resource: their loads return 0 without touching memory.
+    int ld_st = 0, ld_bi = 0;
+    auto load_next = [&](Batch<G, U> &b, uint32_t &bv) {
+        const int tl = (static_cast<int>(blockIdx.x) + ld_st * static_cast<int>(gridDim.x)) * T + ts;
+        const int rows = (ld_st < my_steps && tl < ntiles) ? min(16, N - tl * 16) : 0;
+        const int64_t row0 = static_cast<int64_t>(min(tl, ntiles - 1)) * 16;
+        const int c = cb + ld_bi * U;
         const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t *>(codes + row0 * (K >> 1)), 0, rows * (K >> 1), 0x00020000);
         const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
@@ -375,6 +394,11 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
         const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(zeros + row0 * ngroups), 0, rows * ngroups * 2, 0x00020000);
         load_batch_buf<G, U>(b, crs, srs, zrs, cvo, svo, c, c_last);
+        // bias of column nl (0 without bias: empty resource)
+        const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(bias ? bias + row0 : bias), 0, bias ? rows * 2 : 0, 0x00020000);
+        bv = __builtin_amdgcn_raw_buffer_load_b16(brs, nl * 2, 0, 0);
+        if (++ld_bi == nb) { ld_bi = 0; ++ld_st; }
     };
 
     // x staging, per wave: a wave stages only the K segment it reads (rows
@@ -384,7 +408,54 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
     // each row; the first XR runs are issued ahead of the codes of the first
     // two items, so the wait for x leaves the codes in flight.
     Batch<G, U> b0, b1, b2;
-    {
+    uint32_t bv0, bv1, bv2;
+    if constexpr (NAT) {
+        // one copy per run of 64 pieces along a row; lane l of the run fills
+        // piece position l, i.e. fetches piece l ^ (m % 16) of the run
+        const int seg_pr = (ce - cb) * 16;      // pieces per row of the segment
+        const int rpr = (seg_pr + 63) >> 6;     // runs per row
+        const int k0 = cb * 128;
+        const uint32_t xl0 = lds_address(smem);
+        for (int m = 0; m < M; ++m) {
+            const uint16_t *xrow = x + static_cast<int64_t>(m) * K;
+            for (int q = 0; q < rpr; ++q) {
+                // pieces past K (last chunk) are not copied but cleared below
+                const int kk = k0 + (q * 64 + (lane ^ (m & 15))) * 8;
+                if (q * 64 + lane < seg_pr && kk < K)
+                    lds_dma16(xrow + kk, xl0 + (m * krs + k0) * 2 + q * 1024);
+            }
+        }
+        load_next(b0, bv0);
+        load_next(b1, bv1);
+        // the copies are older than the 2 (2R + U + 1) loads of b0 and b1
+        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * (2 * R + U + 1)) : "memory");
+        if ((K & 127) != 0 && ce == nchunk && ce > cb) {
+            // zero the pieces of the last chunk that lie past K
+            const int p = lane & 15;            // logical piece in the chunk
+            if ((nchunk - 1) * 128 + p * 8 >= K) {
+                for (int m = lane >> 4; m < M; m += 4)
+                    *reinterpret_cast<u32x4 *>(
+                        &xl[m * krs + (nchunk - 1) * 128 + ((p ^ (m & 15)) * 8)]) =
+                        u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+        // group sums of the segment: fragments against ones; lane (nl, kb)
+        // receives rows 4 kb .. 4 kb + 3 (all columns equal)
+        const bf16x8 ones = bf16x8_ones();
+        const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+        for (int cc = cb; cc < ce; ++cc) {
+            f32x4 sg4 = z4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(
+                    reinterpret_cast<const uint8_t *>(xl) + xo[j] + cc * 256);
+                sg4 = mfma16x16x32(as_bf16x8(a), ones, (j % SPG) == 0 ? z4 : sg4);
+                if ((j % SPG) == SPG - 1 && nl == 0)
+                    *reinterpret_cast<f32x4 *>(&xs[(cc * GPC + j / SPG) * MR + 4 * kb]) = sg4;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    } else {
         constexpr int XR = 16;                  // runs per round
         const int seg_pr = (ce - cb) * 16;      // pieces per row of the segment
         const int rpr = (seg_pr + 63) >> 6;     // runs per row
@@ -417,21 +488,20 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
                 const int kk = k0 + p * 8;
                 const bool ok = p < seg_pr;
                 const u32x4 v = xv[j];
-                if (ok) *reinterpret_cast<u32x4 *>(&xl[m * kr + kk]) = interleave8_bf16(v);
+                if (ok) *reinterpret_cast<u32x4 *>(&xl[m * krs + kk]) = interleave8_bf16(v);
                 float sum = (bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y)) +
                             (bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w));
                 // a group's LPG pieces sit in consecutive lanes of one run
                 // (LPG divides 16, runs start at multiples of 512 k), so
                 // they reduce with DPP moves
                 sum = group_sum<LPG>(sum);
-                if (ok && (lane & (LPG - 1)) == 0) xs[(kk / G) * mr + m] = sum;
+                if (ok && (lane & (LPG - 1)) == 0) xs[(kk / G) * MR + m] = sum;
                 if (++q == rpr) { q = 0; ++m; }
             }
         };
         issue(0);
-        // items past the end get an empty resource (nitems >= 1 always)
-        load(b0, 0);
-        load(b1, 1);
+        load_next(b0, bv0);
+        load_next(b1, bv1);
         put(0);
         for (int r0 = XR; r0 < nruns; r0 += XR) {
             issue(r0);
@@ -440,95 +510,344 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
         __builtin_amdgcn_wave_barrier();
     }
 
+    // the outputs of a block step this thread sums (S > 1): T * M * 16 of
+    // them over the block, at most RI per thread
+    constexpr int RI = (T * MR * 16 + NW * 64 - 1) / (NW * 64);
+    bool red_live[RI];
+    int red_slot[RI], red_m[RI], red_nn[RI];
+#pragma unroll
+    for (int it = 0; it < RI; ++it) {
+        const int e = static_cast<int>(threadIdx.x) + it * NW * 64;
+        red_live[it] = e < T * M * 16;
+        red_slot[it] = e / (M * 16);
+        const int rem = e - red_slot[it] * (M * 16);
+        red_m[it] = rem >> 4;
+        red_nn[it] = rem & 15;
+    }
+
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](Batch<G, U> &b, int item) {
-        const int st = item / nb;
-        const int bi = item - st * nb;
+    int sp_st = 0, sp_bi = 0;
+    auto step = [&](Batch<G, U> &b, uint32_t bvr) {
+        const int st = sp_st, bi = sp_bi;
+        if (++sp_bi == nb) { sp_bi = 0; ++sp_st; }
         const int c = cb + bi * U;
-        uint32_t packed[Batch<G, U>::R];
+        // scales and zero-points of the batch as float: s and z - 128 s
+        float svr[R], zzr[R];
 #pragma unroll
-        for (int r = 0; r < Batch<G, U>::R; ++r) packed[r] = (b.s[r] & 0xFFFFu) | (b.z[r] << 16);
+        for (int r = 0; r < R; ++r) {
+            svr[r] = __uint_as_float(b.s[r] << 16);
+            zzr[r] = fmaf(-128.0f, svr[r], __uint_as_float(b.z[r] << 16));
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int cc = c + u;
             if (cc >= ce) break;                // uniform across the wave
             align_groups<G>(b.q[u]);
+            // the chunk's LDS reads first: x fragments, group sums, and the
+            // scale / zero-point of column nl for each group
+            const uint16_t *xc = xa + cc * 128;
+            const float *xsc = xsa + cc * GPC * MR;
+            u32x4 av[4];
+            f32x4 xg[GPC];
+            float sg_[GPC], zg[GPC];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (NAT)
+                    av[j] = *reinterpret_cast<const u32x4 *>(
+                        reinterpret_cast<const uint8_t *>(xl) + xo[j] + cc * 256);
+                else
+                    av[j] = *reinterpret_cast<const u32x4 *>(xc + slot_koff<G>(j, 0) -
+                                                             slot_koff<G>(0, 0));
+            }
+#pragma unroll
+            for (int g = 0; g < GPC; ++g) {
+                const int h = u * GPC + g;      // group of the batch
+                xg[g] = *reinterpret_cast<const f32x4 *>(xsc + g * MR);
+                const int src = (nl * 4 + (h & 3)) * 4;
+                sg_[g] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                       src, __builtin_bit_cast(int, svr[h >> 2])));
+                zg[g] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                      src, __builtin_bit_cast(int, zzr[h >> 2])));
+            }
             f32x4 accg = zero4;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bool first = (j % SPG) == 0;
-                const int ka = cc * 128 + slot_koff<G>(j, kb);
-                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4 *>(&xl[mrow * kr + ka]));
                 uint32_t w[4];
-                unpack8_bias128_il(b.q[u][j], w, uc);
-                accg = mfma16x16x32(a, as_bf16x8(w[0], w[1], w[2], w[3]),
+                if constexpr (NAT)
+                    unpack8_bias128(b.q[u][j], w, uc);
+                else
+                    unpack8_bias128_il(b.q[u][j], w, uc);
+                accg = mfma16x16x32(as_bf16x8(av[j]), as_bf16x8(w[0], w[1], w[2], w[3]),
                                     first ? zero4 : accg);
                 if ((j % SPG) == SPG - 1) {
-                    const uint32_t szv = batch_sz(packed, u * GPC + j / SPG, lane);
-                    const float sv = bf16_lo(szv);
-                    const float zz = fmaf(-128.0f, sv, bf16_hi(szv));
-                    const f32x4 xg = *reinterpret_cast<const f32x4 *>(
-                        &xs[(cc * GPC + j / SPG) * mr + 4 * kq]);
-                    // All four MFMA results are consumed (also for M = 1):
-                    // leaving some of them dead lets the register allocator
-                    // reuse an MFMA destination register while the MFMA is
-                    // still writing it, which gave wrong results.
+                    const int g = j / SPG;
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        acc[i] = fmaf(sv, accg[i], fmaf(zz, xg[i], acc[i]));
+                        acc[i] = fmaf(sg_[g], accg[i], fmaf(zg[g], xg[g][i], acc[i]));
                 }
             }
         }
         if (bi != nb - 1) return;               // end of this block step
+        // bias of column nl, added once per tile (by the waves of K segment 0)
+        if (sg == 0) {
+            const float bvf = bf16_to_f32(static_cast<uint16_t>(bvr));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += bvf;
+        }
         if constexpr (S == 1) {
-            const int col = tile_of(st, ts) * 16 + nl;
+            const int col = ((static_cast<int>(blockIdx.x) + st * static_cast<int>(gridDim.x)) * T + ts) * 16 + nl;
             if (col < N) {
-                const float bv = bias ? bf16_to_f32(bias[col]) : 0.0f;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (4 * kb + i < M)
                         y[static_cast<int64_t>(4 * kb + i) * N + col] =
-                            static_cast<uint16_t>(f32_to_bf16_rne(acc[i] + bv));
+                            static_cast<uint16_t>(f32_to_bf16_rne(acc[i]));
             }
             acc = zero4;
         } else {
             const int par = st & 1;
-            float *rw = red + (static_cast<size_t>(par * NW + wave) * mr) * 16;
+            float *rw = red + (par * NW + wave) * MR * 16;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (4 * kb + i < M) rw[(4 * kb + i) * 16 + nl] = acc[i];
             acc = zero4;
             __syncthreads();
-            for (int e = threadIdx.x; e < T * M * 16; e += NW * 64) {
-                const int slot = e / (M * 16);
-                const int rem = e - slot * (M * 16);
-                const int m = rem >> 4;
-                const int nn = rem & 15;
-                const float *rp = red + (static_cast<size_t>(par * NW + slot * S) * mr + m) * 16 + nn;
+            const int tile0 = (static_cast<int>(blockIdx.x) + st * static_cast<int>(gridDim.x)) * T;
+#pragma unroll
+            for (int it = 0; it < RI; ++it) {
+                if (!red_live[it]) continue;
+                const int slot = red_slot[it], m = red_m[it], nn = red_nn[it];
+                const float *rp = red + ((par * NW + slot * S) * MR + m) * 16 + nn;
                 float sum = 0.f;
 #pragma unroll
-                for (int w = 0; w < S; ++w) sum += rp[w * mr * 16];
-                const int col = tile_of(st, slot) * 16 + nn;
-                if (col < N) {
-                    if (bias) sum += bf16_to_f32(bias[col]);
+                for (int w = 0; w < S; ++w) sum += rp[w * MR * 16];
+                const int col = (tile0 + slot) * 16 + nn;
+                if (col < N)
                     y[static_cast<int64_t>(m) * N + col] =
                         static_cast<uint16_t>(f32_to_bf16_rne(sum));
-                }
             }
         }
     };
 
+    const int nitems = my_steps * nb;
     for (int i = 0; i < nitems; i += 3) {
-        load(b2, i + 2);
-        step(b0, i);
+        load_next(b2, bv2);
+        step(b0, bv0);
         if (i + 1 >= nitems) break;
-        load(b0, i + 3);
-        step(b1, i + 1);
+        load_next(b0, bv0);
+        step(b1, bv1);
         if (i + 2 >= nitems) break;
-        load(b1, i + 4);
-        step(b2, i + 2);
+        load_next(b1, bv1);
+        step(b2, bv2);
+    }
+}
+
+// Persistent split-K kernel for 1 <= M <= 16 whose x fragments come from
+// global memory (L2) instead of LDS: used when x does not fit in LDS. Same
+// (tile, K segment) decomposition and cross-wave reduction as the split
+// kernel; items are 2 chunks; K is a multiple of 128 (no partial chunk
+// whose x would have to read 0 past K). The codes of the next two items and the x
+// fragments of the next one are in flight while an item is computed; loads
+// complete in issue order, so the order codes(t), x(t), codes(t+1), ...
+// lets the wait for x(t) leave codes(t + 1), codes(t + 2) in flight. Group
+// sums come from the matrix cores (fragments against ones); x and the codes
+// are expanded in natural order.
+template <int G, int S>
+__global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_direct_kernel(
+    const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y) {
+    constexpr int NW = GV_SPLIT_WAVES;
+    constexpr int T = NW / S;                   // tiles per block step
+    constexpr int SPG = G / 32;
+    constexpr int GPC = 128 / G;
+    constexpr int U = 2;
+    constexpr int R = Batch<G, U>::R;
+    constexpr int MR = GV_SPLIT_MAX_M;
+    constexpr int OOB = 0x40000000;
+    __shared__ __attribute__((aligned(16))) float red[2][NW][MR][16];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform
+    const int nl = lane & 15;
+    const int kb = lane >> 4;
+    const int ts = wave / S, sg = wave % S;
+    const int nchunk = (K + 127) >> 7;
+    const int ngroups = K / G;
+    const int ntiles = (N + 15) >> 4;
+    const int nsteps = (ntiles + T - 1) / T;
+    const int my_steps = (nsteps - static_cast<int>(blockIdx.x) + gridDim.x - 1) / gridDim.x;
+    const int mrow = nl < M ? nl : M - 1;
+    const Unpack128 uc = unpack128_consts();
+    const bf16x8 ones = bf16x8_ones();
+
+    const int cb = sg * nchunk / S;
+    const int ce = (sg + 1) * nchunk / S;
+    const int c_last = max(cb, ce - 1);
+    const int nb = ((nchunk + S - 1) / S + U - 1) / U;
+
+    const int cvo = nl * (K >> 1) + kb * 16;
+    const int svo = ((lane >> 2) * ngroups + (lane & 3)) * 2;
+    const int xvo = (mrow * K + slot_koff<G>(0, kb)) * 2;     // x byte offset
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(x), 0, M * K * 2, 0x00020000);
+
+    int ld_st = 0, ld_bi = 0;                   // next item whose codes load
+    auto load_codes = [&](Batch<G, U> &b, uint32_t &bv) {
+        const int tl = (static_cast<int>(blockIdx.x) + ld_st * static_cast<int>(gridDim.x)) * T + ts;
+        const int rows = (ld_st < my_steps && tl < ntiles) ? min(16, N - tl * 16) : 0;
+        const int64_t row0 = static_cast<int64_t>(min(tl, ntiles - 1)) * 16;
+        const int c = cb + ld_bi * U;
+        const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(codes + row0 * (K >> 1)), 0, rows * (K >> 1), 0x00020000);
+        const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(scales + row0 * ngroups), 0, rows * ngroups * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(zeros + row0 * ngroups), 0, rows * ngroups * 2, 0x00020000);
+        load_batch_buf<G, U>(b, crs, srs, zrs, cvo, svo, c, c_last);
+        const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(bias ? bias + row0 : bias), 0, bias ? rows * 2 : 0, 0x00020000);
+        bv = __builtin_amdgcn_raw_buffer_load_b16(brs, nl * 2, 0, 0);
+        if (++ld_bi == nb) { ld_bi = 0; ++ld_st; }
+    };
+    int xl_st = 0, xl_bi = 0;                   // next item whose x loads
+    auto load_x = [&](u32x4 (&a)[U][4]) {
+        const bool live = xl_st < my_steps;
+        const int c = cb + xl_bi * U;
+        if (++xl_bi == nb) { xl_bi = 0; ++xl_st; }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int cc = c + u;
+            // chunks outside the segment (or items past the end): nothing
+            const int so = (live && cc < ce) ? cc * 256 : OOB;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                a[u][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                    xrs, xvo, so + (slot_koff<G>(j, 0) - slot_koff<G>(0, 0)) * 2, 0);
+        }
+    };
+
+    // the outputs of a block step this thread sums (S > 1): T * M * 16 of
+    // them over the block, at most RI per thread
+    constexpr int RI = (T * MR * 16 + NW * 64 - 1) / (NW * 64);
+    bool red_live[RI];
+    int red_slot[RI], red_m[RI], red_nn[RI];
+#pragma unroll
+    for (int it = 0; it < RI; ++it) {
+        const int e = static_cast<int>(threadIdx.x) + it * NW * 64;
+        red_live[it] = e < T * M * 16;
+        red_slot[it] = e / (M * 16);
+        const int rem = e - red_slot[it] * (M * 16);
+        red_m[it] = rem >> 4;
+        red_nn[it] = rem & 15;
+    }
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    int sp_st = 0, sp_bi = 0;
+    auto step = [&](Batch<G, U> &b, uint32_t bvr, u32x4 (&a)[U][4]) {
+        const int st = sp_st, bi = sp_bi;
+        if (++sp_bi == nb) { sp_bi = 0; ++sp_st; }
+        const int c = cb + bi * U;
+        float svr[R], zzr[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            svr[r] = __uint_as_float(b.s[r] << 16);
+            zzr[r] = fmaf(-128.0f, svr[r], __uint_as_float(b.z[r] << 16));
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int cc = c + u;
+            if (cc >= ce) break;                // uniform across the wave
+            align_groups<G>(b.q[u]);
+            float sg_[GPC], zg[GPC];
+#pragma unroll
+            for (int g = 0; g < GPC; ++g) {
+                const int h = u * GPC + g;
+                const int src = (nl * 4 + (h & 3)) * 4;
+                sg_[g] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                       src, __builtin_bit_cast(int, svr[h >> 2])));
+                zg[g] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(
+                                                      src, __builtin_bit_cast(int, zzr[h >> 2])));
+            }
+            f32x4 accg = zero4, xsg = zero4;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool first = (j % SPG) == 0;
+                uint32_t w[4];
+                unpack8_bias128(b.q[u][j], w, uc);
+                xsg = mfma16x16x32(as_bf16x8(a[u][j]), ones, first ? zero4 : xsg);
+                accg = mfma16x16x32(as_bf16x8(a[u][j]), as_bf16x8(w[0], w[1], w[2], w[3]),
+                                    first ? zero4 : accg);
+                if ((j % SPG) == SPG - 1) {
+                    const int g = j / SPG;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[i] = fmaf(sg_[g], accg[i], fmaf(zg[g], xsg[i], acc[i]));
+                }
+            }
+        }
+        if (bi != nb - 1) return;               // end of this block step
+        if (sg == 0) {
+            const float bvf = bf16_to_f32(static_cast<uint16_t>(bvr));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] += bvf;
+        }
+        if constexpr (S == 1) {
+            const int col = ((static_cast<int>(blockIdx.x) + st * static_cast<int>(gridDim.x)) * T + ts) * 16 + nl;
+            if (col < N) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * kb + i < M)
+                        y[static_cast<int64_t>(4 * kb + i) * N + col] =
+                            static_cast<uint16_t>(f32_to_bf16_rne(acc[i]));
+            }
+            acc = zero4;
+        } else {
+            const int par = st & 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * kb + i < M) red[par][wave][4 * kb + i][nl] = acc[i];
+            acc = zero4;
+            __syncthreads();
+            const int tile0 = (static_cast<int>(blockIdx.x) + st * static_cast<int>(gridDim.x)) * T;
+#pragma unroll
+            for (int it = 0; it < RI; ++it) {
+                if (!red_live[it]) continue;
+                const int slot = red_slot[it], m = red_m[it], nn = red_nn[it];
+                float sum = 0.f;
+#pragma unroll
+                for (int w = 0; w < S; ++w) sum += red[par][slot * S + w][m][nn];
+                const int col = (tile0 + slot) * 16 + nn;
+                if (col < N)
+                    y[static_cast<int64_t>(m) * N + col] =
+                        static_cast<uint16_t>(f32_to_bf16_rne(sum));
+            }
+        }
+    };
+
+    Batch<G, U> b0, b1, b2;
+    uint32_t bv0, bv1, bv2;
+    u32x4 a0[U][4], a1[U][4], a2[U][4];
+    load_codes(b0, bv0);
+    load_x(a0);
+    load_codes(b1, bv1);
+    const int nitems = my_steps * nb;
+    for (int i = 0; i < nitems; i += 3) {
+        load_x(a1);
+        load_codes(b2, bv2);
+        step(b0, bv0, a0);
+        if (i + 1 >= nitems) break;
+        load_x(a2);
+        load_codes(b0, bv0);
+        step(b1, bv1, a1);
+        if (i + 2 >= nitems) break;
+        load_x(a0);
+        load_codes(b1, bv1);
+        step(b2, bv2, a2);
     }
 }
 
@@ -561,19 +880,23 @@ size_t max_lds_per_block() {
     return lds[dev];
 }
 
+// The split kernel stages x through LDS copies (NAT) from this M on.
+constexpr int GV_NAT_MIN_M = 5;
+
 // Dynamic LDS of the split kernel for (M, K).
 size_t split_lds_bytes(int M, int K, int G) {
     const size_t kr = static_cast<size_t>((K + 127) / 128) * 128;
-    const size_t mr = static_cast<size_t>((M + 3) & ~3);
-    return static_cast<size_t>(M) * kr * 2 + (kr / G) * mr * 4 + 2 * GV_SPLIT_WAVES * mr * 16 * 4;
+    const size_t krs = M >= GV_NAT_MIN_M ? kr : kr + GV_X_PAD;
+    return static_cast<size_t>(M) * krs * 2 + (kr / G) * GV_SPLIT_MAX_M * 4 +
+           2 * GV_SPLIT_WAVES * GV_SPLIT_MAX_M * 16 * 4;
 }
 
-template <int G, int S>
+template <int G, int S, bool NAT>
 hipError_t launch_split_s(const uint16_t *x, int M, const uint8_t *codes,
                           const uint16_t *scales, const uint16_t *zeros,
                           const uint16_t *bias, int N, int K, uint16_t *y,
                           hipStream_t stream) {
-    auto kern = gemv_split_kernel<G, S>;
+    auto kern = gemv_split_kernel<G, S, NAT>;
     static bool attr_set[64] = {false};         // per device
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) dev = 0;
@@ -607,13 +930,52 @@ hipError_t launch_split(const uint16_t *x, int M, const uint8_t *codes,
                         const uint16_t *bias, int N, int K, uint16_t *y,
                         hipStream_t stream) {
     const int nchunk = (K + 127) / 128;
+    if (M >= GV_NAT_MIN_M) {
+        if (nchunk >= 8)
+            return launch_split_s<G, 8, true>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+        if (nchunk >= 4)
+            return launch_split_s<G, 4, true>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+        if (nchunk >= 2)
+            return launch_split_s<G, 2, true>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+        return launch_split_s<G, 1, true>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+    }
     if (nchunk >= 8)
-        return launch_split_s<G, 8>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+        return launch_split_s<G, 8, false>(x, M, codes, scales, zeros, bias, N, K, y, stream);
     if (nchunk >= 4)
-        return launch_split_s<G, 4>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+        return launch_split_s<G, 4, false>(x, M, codes, scales, zeros, bias, N, K, y, stream);
     if (nchunk >= 2)
-        return launch_split_s<G, 2>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-    return launch_split_s<G, 1>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+        return launch_split_s<G, 2, false>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+    return launch_split_s<G, 1, false>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+}
+
+template <int G, int S>
+hipError_t launch_direct_s(const uint16_t *x, int M, const uint8_t *codes,
+                           const uint16_t *scales, const uint16_t *zeros,
+                           const uint16_t *bias, int N, int K, uint16_t *y,
+                           hipStream_t stream) {
+    const int ntiles = (N + 15) / 16;
+    constexpr int T = GV_SPLIT_WAVES / S;
+    const int nsteps = (ntiles + T - 1) / T;
+    const int slots = compute_units();
+    const int blocks = nsteps < slots ? nsteps : slots;
+    gemv_direct_kernel<G, S><<<dim3(blocks), dim3(GV_SPLIT_WAVES * 64), 0, stream>>>(
+        x, M, codes, scales, zeros, bias, N, K, y);
+    return hipGetLastError();
+}
+
+template <int G>
+hipError_t launch_direct(const uint16_t *x, int M, const uint8_t *codes,
+                         const uint16_t *scales, const uint16_t *zeros,
+                         const uint16_t *bias, int N, int K, uint16_t *y,
+                         hipStream_t stream) {
+    const int nchunk = (K + 127) / 128;
+    if (nchunk >= 8)
+        return launch_direct_s<G, 8>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+    if (nchunk >= 4)
+        return launch_direct_s<G, 4>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+    if (nchunk >= 2)
+        return launch_direct_s<G, 2>(x, M, codes, scales, zeros, bias, N, K, y, stream);
+    return launch_direct_s<G, 1>(x, M, codes, scales, zeros, bias, N, K, y, stream);
 }
 
 template <int G>
@@ -625,6 +987,8 @@ hipError_t launch_gemv_g(const uint16_t *x, int M, const uint8_t *codes,
     if (M <= GV_SPLIT_MAX_M && split_lds_bytes(M, K, G) <= max_lds_per_block()) {
         return launch_split<G>(x, M, codes, scales, zeros, bias, N, K, y, stream);
     }
+    if (M <= GV_SPLIT_MAX_M && K % 128 == 0)
+        return launch_direct<G>(x, M, codes, scales, zeros, bias, N, K, y, stream);
     gemv_phased_kernel<G, GV_WAVES><<<dim3(ntiles), dim3(GV_WAVES * 64), 0, stream>>>(
         x, M, codes, scales, zeros, bias, N, K, y);
     return hipGetLastError();

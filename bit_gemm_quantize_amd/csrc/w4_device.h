@@ -151,6 +151,21 @@ __device__ __forceinline__ bf16x8 bf16x8_ones() {
     return as_bf16x8(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
 }
 
+// 16 bytes per lane, global -> LDS: lane l writes LDS byte address lds
+// (wave-uniform) + 16 l; inactive lanes write nothing. No output registers:
+// the caller waits with an explicit s_waitcnt vmcnt before reading LDS.
+__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 : : "v"(g), "s"(lds) : "memory", "m0");
+}
+
+// LDS byte address of a __shared__ object.
+template <typename P>
+__device__ __forceinline__ uint32_t lds_address(P *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (__attribute__((address_space(3))) const uint8_t *)(p)));
+}
+
 // D = A(16x32) * B(32x16) + C on the bf16 matrix cores.
 // Lane l supplies A[l%16][8*(l/16) .. +8) and B[8*(l/16) .. +8)[l%16];
 // it receives D[4*(l/16) + i][l%16] in element i.

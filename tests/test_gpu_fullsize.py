@@ -53,6 +53,26 @@ def test_llama3_8b_m16_outliers(w4, layer, G):
                     what=f"llama {layer} M=16 G={G}", strict=True)
 
 
+@pytest.mark.parametrize("M", [1, 4])
+@pytest.mark.parametrize("G", [32, 64])
+@pytest.mark.parametrize("layer", sorted(workloads.LLAMA3_8B))
+def test_llama3_8b_small_m_repeat(w4, layer, G, M):
+    # Several (tile, K segment) items per wave on the wide layers; two calls
+    # must agree bit for bit (a register hazard once made them differ) and
+    # match the oracle.
+    N, K = workloads.LLAMA3_8B[layer]
+    (cd, sd, zd), (c, s, z) = quant_full(w4, 2, layer, G)
+    x = workloads.activation_bits(5, M, K)
+    xd = gu.to_dev_bf16(x)
+    y1 = w4.w4a16_linear(xd, cd, sd, zd, G)
+    y2 = w4.w4a16_linear(xd, cd, sd, zd, G)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2), f"llama {layer} M={M} G={G}: two calls differ"
+    y_ref = oracle.linear_ref(x, c, s, z, G)
+    gu.check_linear(gu.to_host_bits(y1), y_ref, gu.abs_bound(x, c, s, z, G),
+                    what=f"llama {layer} M={M} G={G}", strict=True)
+
+
 @pytest.mark.parametrize("layer", sorted(workloads.GEMMA3_12B))
 def test_gemma3_12b_prefill_m2048(w4, layer):
     N, K = workloads.GEMMA3_12B[layer]

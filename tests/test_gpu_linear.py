@@ -68,6 +68,19 @@ def test_gemv(w4, G, M, shape):
     run_case(w4, M, N, K, G, bias=(M % 2 == 1), path=gu_path(w4, "GEMV"), seed=N + K + M)
 
 
+# Long rows: x of M rows no longer fits in LDS for the larger M, which
+# moves the decode path to the kernels that read x fragments from L2 (K a
+# multiple of 128) or stage it in phases (otherwise).
+LONG_K_CASES = [(16, 40, 10240, 32), (16, 40, 10240, 64), (16, 40, 10240, 128),
+                (16, 40, 10016, 32), (16, 40, 10048, 64), (6, 72, 16384, 128),
+                (4, 40, 16512, 128), (2, 24, 32768, 64), (9, 33, 12288, 32)]
+
+
+@pytest.mark.parametrize("M,N,K,G", LONG_K_CASES)
+def test_gemv_long_k(w4, M, N, K, G):
+    run_case(w4, M, N, K, G, bias=(K % 3 == 1), path=gu_path(w4, "GEMV"), seed=M + N + K)
+
+
 GEMM_SHAPES = [(16, 64), (130, 320), (257, 512), (64, 96)]
 
 
