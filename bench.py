@@ -318,7 +318,7 @@ def main():
         set_ms = time_graphs(torch, [g], max(2, reps // 2)) / n_g
         del g
         out["gemv_m1"] = {
-            "kernel": "gemv_split_kernel<128, 8>", "bound": "hbm",
+            "kernel": "gemv_split_kernel<128, 8, false>", "bound": "hbm",
             "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
             "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
             "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -354,7 +354,7 @@ def main():
             tot_b += b
             del g, copies, fns
         out["gemv_m16_g32"] = {
-            "kernel": "gemv_phased_kernel<32, 8>", "bound": "hbm",
+            "kernel": "gemv_split_kernel<32, 8, true> (qkv, o, gate_up), gemv_direct_kernel<32, 8> (down)", "bound": "hbm",
             "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
             "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_per_set": tot_b, "per_layer": per,
