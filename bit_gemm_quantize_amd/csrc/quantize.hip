@@ -14,8 +14,10 @@
 // chunk number times 8 bytes. A group is G/16 consecutive lanes (2, 4 or 8,
 // aligned inside a DPP row), which reduce min/max with DPP ops.
 //
-// Exactness: the scale uses a correctly rounded binary32 divide (built with
-// correctly rounded division; no fp contraction in this file). Codes use
+// Exactness: the scale is the correctly rounded binary32 quotient (a
+// multiply by RN(1/15) and one fma correction, which reproduces the IEEE
+// divide for every positive finite range; no fp contraction in this file).
+// Codes use
 // t = w * rcp(s) - lo * rcp(s) (one fma): with s in [2^-100, 2^100] the
 // hardware reciprocal is within 1 ulp, so t is within 15.06 * 2^-21 plus the
 // rounding of lo * rcp(s) of the correctly rounded quotient. When every t of
@@ -114,7 +116,11 @@ __device__ __forceinline__ void quantize16(const u32x4 d0, const u32x4 d1, int64
     const float lo = mn + 0.0f;                // -0 -> +0
     const float hi = mx + 0.0f;
     const float range = hi - lo;
-    const float s32 = range / 15.0f;           // correctly rounded
+    // range / 15 correctly rounded: q0 = range * RN(1/15) and one fma
+    // correction (equal to the IEEE quotient for every positive finite
+    // binary32 range, denormals included; checked exhaustively)
+    const float q0 = range * (1.0f / 15.0f);
+    const float s32 = fmaf(fmaf(-15.0f, q0, range), 1.0f / 15.0f, q0);
     const uint32_t sb = f32_to_bf16_rne(s32);
     const float s = __uint_as_float(sb << 16);
     const uint32_t zb = __float_as_uint(lo) >> 16;
