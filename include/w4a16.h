@@ -34,8 +34,10 @@
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream).
  *     A launch failure returns W4_ERR_HIP; faults during execution surface
  *     at the caller's next synchronisation, as for any HIP kernel.
- *   - The library keeps no state between calls and allocates no memory;
- *     calls are reentrant. No C++ exception crosses the interface.
+ *   - The library allocates no memory and keeps no per-call state (it
+ *     caches a few device attributes per device, set once, and the LDS
+ *     limit of one kernel); calls are reentrant. No C++ exception crosses
+ *     the interface.
  */
 #ifndef W4A16_H
 #define W4A16_H
