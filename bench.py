@@ -179,7 +179,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "step", "gemv", "gemv16", "gemm", "quantize", "copy"],
+    ap.add_argument("--only", choices=["all", "step", "gemv", "gemv16", "gemm", "quantize", "fake",
+                                       "copy"],
                     default="all", help="restrict to one part (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -272,12 +273,38 @@ def main():
             tot_ms += ms
             del g
         out["quantize"] = {
-            "kernel": "quantize_kernel<128>", "bound": "hbm",
+            "kernel": "quantize_kernel<128, false>", "bound": "hbm",
             "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
             "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
             "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_per_set": tot_b, "set_us": round(tot_ms * 1e3, 3),
             "per_layer": per,
+        }
+
+    # ---- fake-quantize round trip (QAT forward weight), G = 32 ------------
+    if args.only in ("all", "fake"):
+        GF = 32
+        per = {}
+        tot_b = 0
+        tot_ms = 0.0
+        for name, (N, K) in layers.items():
+            wout = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+            fns = [(lambda e=e, n=name, o=wout: w4.fake_quant_int4_grouped(e[n][0], GF, out=o))
+                   for e in sets]
+            for f in fns:
+                f()
+            g = graph_of(torch, fns)
+            ms = time_graphs(torch, [g], max(2, reps // n_sets)) / n_sets
+            b = 4 * N * K                   # read W, write W_hat (bf16 each)
+            per[name] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1)}
+            tot_b += b
+            tot_ms += ms
+            del g, wout, fns
+        out["fake_quant_g32"] = {
+            "kernel": "quantize_kernel<32, true>", "bound": "hbm",
+            "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
+            "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_set": tot_b, "set_us": round(tot_ms * 1e3, 3), "per_layer": per,
         }
 
     # ---- decode GEMV on its own over rotating quantized copies ----------

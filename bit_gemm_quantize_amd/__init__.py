@@ -16,7 +16,7 @@ from .build import LIB_PATH
 
 __all__ = [
     "W4Status", "W4Path", "W4Error", "GROUP_SIZES", "GEMV_MAX_M", "lib",
-    "quantize_int4_grouped", "w4a16_linear", "status_string",
+    "quantize_int4_grouped", "fake_quant_int4_grouped", "w4a16_linear", "status_string",
 ]
 
 GROUP_SIZES = (32, 64, 128)
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.quantize_int4_grouped.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p, _p]
         L.quantize_int4_grouped.restype = _int
+        L.fake_quant_int4_grouped.argtypes = [_p, _i64, _i64, _i64, _p, _p]
+        L.fake_quant_int4_grouped.restype = _int
         L.w4a16_linear.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p]
         L.w4a16_linear.restype = _int
         L.w4a16_linear_select.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
@@ -129,6 +131,25 @@ def quantize_int4_grouped(W, G: int, codes=None, scales=None, zeros=None):
     if st != W4Status.OK:
         raise W4Error(st, "quantize_int4_grouped")
     return codes, scales, zeros
+
+
+def fake_quant_int4_grouped(W, G: int, out=None):
+    """Quantize -> dequantize round trip of a bf16 GPU weight W[N, K] (group
+    size G along K): returns bf16 [N, K] (allocated when ``out`` is None).
+    Enqueued on torch's current stream."""
+    torch = _torch()
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [N, K]")
+    N, K = W.shape
+    _check(W, "W", torch.bfloat16, (N, K))
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=W.device)
+    _check(out, "out", torch.bfloat16, (N, K), W.device)
+    st = lib().fake_quant_int4_grouped(W.data_ptr(), N, K, G, out.data_ptr(),
+                                       _stream_ptr(W.device))
+    if st != W4Status.OK:
+        raise W4Error(st, "fake_quant_int4_grouped")
+    return out
 
 
 def w4a16_linear(x, codes, scales, zeros, G: int, bias=None, out=None,

@@ -87,6 +87,17 @@ w4_status quantize_int4_grouped(const uint16_t *W, int64_t N, int64_t K, int64_t
     return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
 
+w4_status fake_quant_int4_grouped(const uint16_t *W, int64_t N, int64_t K, int64_t G,
+                                  uint16_t *W_hat, hipStream_t stream) {
+    if (!W || !W_hat) return W4_ERR_NULL;
+    const w4_status st = check_nkg(N, K, G);
+    if (st != W4_OK) return st;
+    if (!aligned16(W) || !aligned16(W_hat)) return W4_ERR_ALIGN;
+    if (overlap(W_hat, 2 * N * K, W, 2 * N * K)) return W4_ERR_ALIAS;
+    const hipError_t e = w4::launch_fake_quant(W, N, K, static_cast<int>(G), W_hat, stream);
+    return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
 w4_status w4a16_linear(const uint16_t *x, int64_t M, const uint8_t *codes,
                        const uint16_t *scales, const uint16_t *zeros,
                        const uint16_t *bias, int64_t N, int64_t K, int64_t G,

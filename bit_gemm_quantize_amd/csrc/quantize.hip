@@ -78,12 +78,15 @@ W4_DPP_MINMAX(max_hmirror, "v_max_f32_dpp", "row_half_mirror")
 #undef W4_DPP_MINMAX
 
 // One lane quantizes 16 consecutive elements (two 16-byte loads); a group is
-// G/16 consecutive lanes (2, 4 or 8 inside one DPP row).
-template <int G>
+// G/16 consecutive lanes (2, 4 or 8 inside one DPP row). FAKE: instead of
+// codes, scales and zero-points, write the dequantized weights
+// bf16_rne(fl32(q s + z)) (32 bytes per lane).
+template <int G, bool FAKE>
 __device__ __forceinline__ void quantize16(const u32x4 d0, const u32x4 d1, int64_t c,
                                           u32x2 *__restrict__ codes,
                                           uint16_t *__restrict__ scales,
-                                          uint16_t *__restrict__ zeros) {
+                                          uint16_t *__restrict__ zeros,
+                                          u32x4 *__restrict__ what) {
     constexpr int LPG = G / 16;
     float v[16];
     const uint32_t w[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
@@ -126,6 +129,9 @@ __device__ __forceinline__ void quantize16(const u32x4 d0, const u32x4 d1, int64
     const uint32_t zb = __float_as_uint(lo) >> 16;
 
     uint32_t out0 = 0, out1 = 0;
+    float q[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) q[i] = 0.0f;
     if (s != 0.0f) {
         // Fast path: t = w * r + c with r = rcp(s), c = -lo * r. Its error
         // against fl(fl(w - lo) / s) is below 15.06 * 2^-21 + |c| * 2^-23, so
@@ -136,7 +142,6 @@ __device__ __forceinline__ void quantize16(const u32x4 d0, const u32x4 d1, int64
         const float cst = -lo * r;
         const bool extreme = !(s >= 0x1p-100f && s <= 0x1p100f);
         const float margin = 0.5f - (0x1p-16f + fabsf(cst) * 0x1p-22f);
-        float q[16];
         float dmax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
@@ -151,13 +156,28 @@ __device__ __forceinline__ void quantize16(const u32x4 d0, const u32x4 d1, int64
             for (int i = 0; i < 16; ++i)
                 q[i] = fminf(fmaxf(__builtin_rintf((v[i] - lo) / s), 0.0f), 15.0f);
         }
-        // bytes q[2j] + 16 q[2j+1] (exact small integers), four per dword;
-        // a fast-path q may be -0 (t a hair below 0), which converts to 0
+        if constexpr (!FAKE) {
+            // bytes q[2j] + 16 q[2j+1] (exact small integers), four per
+            // dword; a fast-path q may be -0 (t a hair below 0): it converts
+            // to 0
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            out0 = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(16.0f, q[2 * j + 1], q[2 * j]), j, out0);
-            out1 = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(16.0f, q[2 * j + 9], q[2 * j + 8]), j, out1);
+            for (int j = 0; j < 4; ++j) {
+                out0 = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(16.0f, q[2 * j + 1], q[2 * j]), j, out0);
+                out1 = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(16.0f, q[2 * j + 9], q[2 * j + 8]), j, out1);
+            }
         }
+    }
+    if constexpr (FAKE) {
+        // q s is exact (4-bit q, bf16 s), so fma(q, s, z) is fl32(q s + z);
+        // a fast-path q of -0 gives z exactly
+        uint32_t o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            o[j] = f32_to_bf16_rne(fmaf(q[2 * j], s, lo)) |
+                   (f32_to_bf16_rne(fmaf(q[2 * j + 1], s, lo)) << 16);
+        __builtin_nontemporal_store(u32x4{o[0], o[1], o[2], o[3]}, what + 2 * c);
+        __builtin_nontemporal_store(u32x4{o[4], o[5], o[6], o[7]}, what + 2 * c + 1);
+        return;
     }
     __builtin_nontemporal_store(u32x2{out0, out1}, codes + c);
     // The first lane of each group stores the group's scale and zero-point
@@ -170,10 +190,10 @@ __device__ __forceinline__ void quantize16(const u32x4 d0, const u32x4 d1, int64
     }
 }
 
-template <int G>
+template <int G, bool FAKE>
 __global__ __launch_bounds__(QT_THREADS) void quantize_kernel(
     const u32x4 *__restrict__ W, int64_t nchunk, u32x2 *__restrict__ codes,
-    uint16_t *__restrict__ scales, uint16_t *__restrict__ zeros) {
+    uint16_t *__restrict__ scales, uint16_t *__restrict__ zeros, u32x4 *__restrict__ what) {
     // nchunk counts 16-element chunks; a thread takes chunks c, c + stride,
     // ... and loads the next one before quantizing the current one. Every
     // chunk of a group shares the in/out-of-range decision (nchunk and the
@@ -195,23 +215,25 @@ __global__ __launch_bounds__(QT_THREADS) void quantize_kernel(
     load(a0, a1, c);
     int64_t c1 = c + stride;
     load(b0, b1, c1);
-    quantize16<G>(a0, a1, c, codes, scales, zeros);
+    quantize16<G, FAKE>(a0, a1, c, codes, scales, zeros, what);
     while (c1 < nchunk) {
         const int64_t c2 = c1 + stride;
         load(a0, a1, c2);
-        quantize16<G>(b0, b1, c1, codes, scales, zeros);
+        quantize16<G, FAKE>(b0, b1, c1, codes, scales, zeros, what);
         if (c2 >= nchunk) break;
         c1 = c2 + stride;
         load(b0, b1, c1);
-        quantize16<G>(a0, a1, c2, codes, scales, zeros);
+        quantize16<G, FAKE>(a0, a1, c2, codes, scales, zeros, what);
     }
 }
 
 } // namespace
 
-hipError_t launch_quantize(const uint16_t *W, int64_t N, int64_t K, int G,
-                           uint8_t *codes, uint16_t *scales, uint16_t *zeros,
-                           hipStream_t stream) {
+namespace {
+
+template <bool FAKE>
+hipError_t launch_q(const uint16_t *W, int64_t N, int64_t K, int G, uint8_t *codes,
+                    uint16_t *scales, uint16_t *zeros, uint16_t *what, hipStream_t stream) {
     const int64_t nchunk = N * K / 16;
     int64_t blocks = (nchunk + QT_THREADS * QT_UNROLL - 1) / (QT_THREADS * QT_UNROLL);
     const int64_t max_blocks = 256 * 8;        // 8 blocks per compute unit
@@ -219,13 +241,27 @@ hipError_t launch_quantize(const uint16_t *W, int64_t N, int64_t K, int G,
     const dim3 grid(static_cast<unsigned>(blocks)), block(QT_THREADS);
     const u32x4 *w4p = reinterpret_cast<const u32x4 *>(W);
     u32x2 *c64 = reinterpret_cast<u32x2 *>(codes);
+    u32x4 *wh = reinterpret_cast<u32x4 *>(what);
     switch (G) {
-    case 32: quantize_kernel<32><<<grid, block, 0, stream>>>(w4p, nchunk, c64, scales, zeros); break;
-    case 64: quantize_kernel<64><<<grid, block, 0, stream>>>(w4p, nchunk, c64, scales, zeros); break;
-    case 128: quantize_kernel<128><<<grid, block, 0, stream>>>(w4p, nchunk, c64, scales, zeros); break;
+    case 32: quantize_kernel<32, FAKE><<<grid, block, 0, stream>>>(w4p, nchunk, c64, scales, zeros, wh); break;
+    case 64: quantize_kernel<64, FAKE><<<grid, block, 0, stream>>>(w4p, nchunk, c64, scales, zeros, wh); break;
+    case 128: quantize_kernel<128, FAKE><<<grid, block, 0, stream>>>(w4p, nchunk, c64, scales, zeros, wh); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_quantize(const uint16_t *W, int64_t N, int64_t K, int G,
+                           uint8_t *codes, uint16_t *scales, uint16_t *zeros,
+                           hipStream_t stream) {
+    return launch_q<false>(W, N, K, G, codes, scales, zeros, nullptr, stream);
+}
+
+hipError_t launch_fake_quant(const uint16_t *W, int64_t N, int64_t K, int G, uint16_t *what,
+                             hipStream_t stream) {
+    return launch_q<true>(W, N, K, G, nullptr, nullptr, nullptr, what, stream);
 }
 
 } // namespace w4

@@ -11,6 +11,10 @@ hipError_t launch_quantize(const uint16_t *W, int64_t N, int64_t K, int G,
                            uint8_t *codes, uint16_t *scales, uint16_t *zeros,
                            hipStream_t stream);
 
+// Quantize -> dequantize round trip of launch_quantize, bf16 out.
+hipError_t launch_fake_quant(const uint16_t *W, int64_t N, int64_t K, int G, uint16_t *what,
+                             hipStream_t stream);
+
 // Decode GEMV, 1 <= M <= 16.
 hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *codes,
                        const uint16_t *scales, const uint16_t *zeros,

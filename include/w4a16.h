@@ -98,6 +98,30 @@ w4_status quantize_int4_grouped(const uint16_t *W, int64_t N, int64_t K,
                                 uint16_t *zeros, hipStream_t stream);
 
 /*
+ * fake_quant_int4_grouped - the quantize -> dequantize round trip of
+ * quantize_int4_grouped, in bf16: the weight a quantization-aware training
+ * forward uses to simulate int4 weight quantization (torchao README
+ * ("PyTorch原生训练至推理模型优化"), "Training / quantization-aware
+ * training": prepare / convert steps over a group-wise int4 weight config;
+ * "torchao模型量化完全指南" section 4.1: QAT simulates the quantization error
+ * during training; torchao release notes, "BC Breaking": the int4 weight
+ * fake-quantize config).
+ *
+ * For every element, with q, s, z exactly as quantize_int4_grouped computes
+ * them (same group, same binary32 steps):
+ *   W_hat[n][k] = bf16_rne( fl32( q[n][k] * s[n][g] + z[n][g] ) )
+ * (q * s is exact in binary32, so this is one fused multiply-add, then the
+ * round to bf16). Bit-exact and deterministic for the inputs
+ * quantize_int4_grouped accepts; constant groups come back unchanged.
+ *
+ * W       in   bf16 [N, K], read only
+ * N, K, G in   as for quantize_int4_grouped
+ * W_hat   out  bf16 [N, K]; must not overlap W
+ */
+w4_status fake_quant_int4_grouped(const uint16_t *W, int64_t N, int64_t K, int64_t G,
+                                  uint16_t *W_hat, hipStream_t stream);
+
+/*
  * w4a16_linear - y = x . w_hat^T (+ bias), the bf16-int4 mixed-precision
  * linear ("Optimum Quanto": accelerated bf16-int4 matmul; accumulation wider
  * than the inputs, then dequantization; bias kept in float).

@@ -1,5 +1,5 @@
-"""CPU oracle for group-wise asymmetric int4 weight-only quantization and
-the W4A16 linear layer.
+"""CPU oracle for group-wise asymmetric int4 weight-only quantization, its
+fake-quantize round trip, and the W4A16 linear layer.
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
 execute this package: only the test suite, the smoke check and the CPU
@@ -13,6 +13,7 @@ from .ref import (  # noqa: F401
     quantize_ref,
     unpack_codes_ref,
     dequant_ref,
+    fake_quant_ref,
     linear_ref,
     linear_rows_ref,
     rel_frobenius,

@@ -23,7 +23,11 @@ Sources (web pages; cited by title and section):
     [1, 512] input; group sizes 32 or 64 recommended, smaller is more accurate.
   * torchao README page ("PyTorch原生训练至推理模型优化"), quick start:
     group-wise int4 weight-only config with ``group_size``; "plain" packing
-    format for int4.
+    format for int4. Same page, "Training / quantization-aware training":
+    a group-wise int4 weight config applied in a "prepare" and a "convert"
+    step; "torchao模型量化完全指南" section 4.1: QAT simulates the
+    quantization error during training; the torchao release notes page,
+    "BC Breaking": the int4 weight fake-quantize config.
 
 Readings taken where the pages leave the step open (each is listed in the
 design notes of the repository):
@@ -47,6 +51,10 @@ design notes of the repository):
       unrounded; the product rounds its fp32 result to bf16.
   R10 inputs must be finite and every group range hi - lo must be finite in
       float32 (the pages say nothing about non-finite weights).
+  R16 fake quantization (the quantize -> dequantize round trip a QAT forward
+      uses) returns bf16_rne( fl32( q * s + z ) ) per element, with q, s, z
+      exactly as the quantizer computes them: the dequantization in binary32
+      like every other step, then rounded to the bf16 weight dtype.
 """
 from __future__ import annotations
 
@@ -168,6 +176,25 @@ def dequant_ref(codes, scales_bits, zeros_bits, G: int) -> np.ndarray:
     if s.shape != (N, K // G) or z.shape != (N, K // G):
         raise ValueError("scales/zeros must be [N, K/G]")
     return q * np.repeat(s, G, axis=1) + np.repeat(z, G, axis=1)
+
+
+def fake_quant_ref(W_bits: np.ndarray, G: int) -> np.ndarray:
+    """Quantize -> dequantize round trip of a bf16 weight W[N, K] (R16).
+
+    torchao README, "Training / quantization-aware training", and
+    "torchao模型量化完全指南" section 4.1: the training forward sees the
+    weight with the quantization error simulated. Steps: quantize_ref's
+    q, s, z; then, in binary32, q * s (exact: a 4-bit integer times a bf16
+    value) plus z (one rounding); then round to bf16 (nearest, ties to even).
+    Returns uint16 bf16 bits [N, K].
+    """
+    codes, s_bits, z_bits = quantize_ref(W_bits, G)
+    q = unpack_codes_ref(codes).astype(np.float32)
+    s = np.repeat(bf16_bits_to_f32(s_bits), G, axis=1)
+    z = np.repeat(bf16_bits_to_f32(z_bits), G, axis=1)
+    prod = (q * s).astype(np.float32)
+    w = (prod + z).astype(np.float32)
+    return f32_to_bf16_bits(w)
 
 
 # ---------------------------------------------------------------------------

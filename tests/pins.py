@@ -223,6 +223,34 @@ def check_bf16_helper(f32_to_bf16_bits):
     assert np.array_equal(f32_to_bf16_bits(x), theirs), "bf16 rounding"
 
 
+# --- pin 6: the fake-quantize round trip --------------------------------------
+
+def check_fake_quant(fake_quant, quantize, W_bits, G):
+    """Every element within half a step (plus the roundings to binary32 and
+    bf16) of its weight; constant groups unchanged; and the same bits as an
+    independent evaluation: torch float64 q * s + z rounded by torch to
+    float32 and then to bf16."""
+    N, K = W_bits.shape
+    fq = fake_quant(W_bits, G)
+    assert fq.shape == (N, K) and fq.dtype == np.uint16
+    codes, s_bits, z_bits = quantize(W_bits, G)
+    q = unpack_test(codes).astype(np.float64)
+    s = np.repeat(f32_from_bf16(s_bits).astype(np.float64), G, axis=1)
+    z = np.repeat(f32_from_bf16(z_bits).astype(np.float64), G, axis=1)
+    exact = q * s + z
+    theirs = (torch.from_numpy(exact).to(torch.float32).to(torch.bfloat16)
+              .view(torch.int16).numpy().view(np.uint16))
+    assert np.array_equal(fq, theirs), "fake quant != torch rounding of q s + z"
+    w = f32_from_bf16(W_bits).astype(np.float64)
+    got = f32_from_bf16(fq).astype(np.float64)
+    bound = s / 2 + np.abs(got) * 2.0**-8 + np.abs(exact) * 2.0**-24 + 1e-300
+    assert np.all(np.abs(got - w) <= bound), "fake quant further than s/2 from w"
+    wg = w.reshape(N, K // G, G)
+    const = np.all(wg == wg[:, :, :1], axis=2)
+    cmask = np.repeat(const, G, axis=1)
+    assert np.array_equal(got[cmask], w[cmask] + 0.0), "constant group changed"
+
+
 def run_all_pins(mod):
     """Every pin against an oracle module-like object."""
     check_bf16_helper(mod.f32_to_bf16_bits)
@@ -237,3 +265,7 @@ def run_all_pins(mod):
         check_invariants(mod.quantize_ref, mod.dequant_ref, bf16_from_float(V), G)
     check_grid_exact(mod.quantize_ref, mod.dequant_ref, mod.linear_ref,
                      3, 24, 256, 64, seed=9, with_bias=True)
+    if hasattr(mod, "fake_quant_ref"):
+        V = rng.standard_normal((8, 256)) * 10.0 ** rng.integers(-3, 3, (8, 1))
+        V[2, :32] = -1.5
+        check_fake_quant(mod.fake_quant_ref, mod.quantize_ref, bf16_from_float(V), 32)

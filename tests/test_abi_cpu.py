@@ -30,8 +30,8 @@ def declared_functions():
 
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
-        "quantize_int4_grouped", "w4a16_linear", "w4a16_linear_select",
-        "w4_status_string"])
+        "quantize_int4_grouped", "fake_quant_int4_grouped", "w4a16_linear",
+        "w4a16_linear_select", "w4_status_string"])
 
 
 def test_library_exports_every_declared_function(L):
@@ -82,6 +82,26 @@ def q(L, W=A, N=64, K=128, G=32, codes=B, s=C, z=D):
 ])
 def test_quantize_validation(L, kw, expect):
     assert q(L, **kw) == expect
+
+
+def fq(L, W=A, N=64, K=128, G=32, out=B):
+    return L.fake_quant_int4_grouped(W, N, K, G, out, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(W=None), w4.W4Status.ERR_NULL),
+    (dict(out=None), w4.W4Status.ERR_NULL),
+    (dict(N=0), w4.W4Status.ERR_SHAPE),
+    (dict(K=-128), w4.W4Status.ERR_SHAPE),
+    (dict(G=96), w4.W4Status.ERR_GROUP),
+    (dict(K=160, G=64), w4.W4Status.ERR_SHAPE),
+    (dict(W=A + 2), w4.W4Status.ERR_ALIGN),
+    (dict(out=B + 8), w4.W4Status.ERR_ALIGN),
+    (dict(out=A), w4.W4Status.ERR_ALIAS),                     # in place
+    (dict(out=A + 64 * 128 * 2 - 16), w4.W4Status.ERR_ALIAS),  # tail overlap
+])
+def test_fake_quant_validation(L, kw, expect):
+    assert fq(L, **kw) == expect
 
 
 def lin(L, x=A, M=4, codes=B, s=C, z=D, bias=None, N=64, K=128, G=32, y=E, path=0):

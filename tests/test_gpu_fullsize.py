@@ -53,6 +53,16 @@ def test_llama3_8b_m16_outliers(w4, layer, G):
                     what=f"llama {layer} M=16 G={G}", strict=True)
 
 
+@pytest.mark.parametrize("layer", ["o", "down"])
+def test_llama3_8b_fake_quant_g32(w4, layer):
+    W = workloads.weight_bits(2, layer)
+    gu.log(f"full fake quant layer={layer} shape={W.shape} G=32")
+    got = gu.to_host_bits(w4.fake_quant_int4_grouped(gu.to_dev_bf16(W), 32))
+    torch.cuda.synchronize()
+    ref = oracle.fake_quant_ref(W, 32)
+    assert np.array_equal(got, ref), f"{layer}: {int((got != ref).sum())} elements differ"
+
+
 @pytest.mark.parametrize("M", [1, 4])
 @pytest.mark.parametrize("G", [32, 64])
 @pytest.mark.parametrize("layer", sorted(workloads.LLAMA3_8B))

@@ -70,6 +70,35 @@ def test_quantize_bit_exact_distributions(w4, G, dist):
 
 
 @pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("dist", DISTS)
+def test_fake_quant_bit_exact_distributions(w4, G, dist):
+    import torch
+    N, K = 29, 4 * 128 + (G if G < 128 else 0)
+    W = _dist(dist, N, K, seed=500 + G + DISTS.index(dist))
+    gu.log(f"fake quant dist={dist} G={G} N={N} K={K}")
+    out = gu.Guarded((N, K), torch.bfloat16)
+    w4.fake_quant_int4_grouped(gu.to_dev_bf16(W), G, out=out.tensor)
+    torch.cuda.synchronize()
+    out.check_guards()
+    got = gu.to_host_bits(out.tensor)
+    ref = oracle.fake_quant_ref(W, G)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{dist} G={G}: {len(bad)} elements differ, first {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+@pytest.mark.parametrize("N,Kmul", [(1, 1), (3, 7), (130, 2)])
+def test_fake_quant_shapes(w4, G, N, Kmul):
+    import torch
+    K = G * Kmul
+    W = workloads.random_bf16((N, K), 0.02, seed=N * 17 + K)
+    gu.log(f"fake quant shape N={N} K={K} G={G}")
+    got = gu.to_host_bits(w4.fake_quant_int4_grouped(gu.to_dev_bf16(W), G))
+    torch.cuda.synchronize()
+    assert np.array_equal(got, oracle.fake_quant_ref(W, G))
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
 @pytest.mark.parametrize("N,Kmul", [(1, 1), (1, 3), (2, 1), (7, 5), (16, 8), (129, 3),
                                     (1000, 2), (3, 64)])
 def test_quantize_bit_exact_shapes(w4, G, N, Kmul):

@@ -119,6 +119,35 @@ def test_invariants_outlier_columns():
     pins.check_invariants(oracle.quantize_ref, oracle.dequant_ref, W, G)
 
 
+# --- fake quantization (quantize -> dequantize round trip) ----------------------
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_fake_quant_many_magnitudes(G):
+    rng = np.random.default_rng(200 + G)
+    blocks = [rng.standard_normal((6, 4 * G)) * mag
+              for mag in (1e-30, 1e-8, 0.02, 1.0, 1e3, 1e30)]
+    v = np.concatenate(blocks)
+    v[1, :G] = 0.7                                  # constant group
+    v[4, G:2 * G] = -2.5                            # constant negative group
+    v[7, 3] *= 400.0                                # single outlier
+    pins.check_fake_quant(oracle.fake_quant_ref, oracle.quantize_ref,
+                          pins.bf16_from_float(v), G)
+
+
+def test_fake_quant_outlier_columns():
+    import workloads
+    K, G = 512, 32
+    cols = workloads.outlier_columns(K, 4)
+    W = workloads.normal_bf16_rows(48, K, 0.02, 4, outlier_cols=cols)
+    pins.check_fake_quant(oracle.fake_quant_ref, oracle.quantize_ref, W, G)
+
+
+@pytest.mark.parametrize("G", [32, 128])
+def test_fake_quant_grid_weights_come_back_unchanged(G):
+    W, _, _, _ = pins.grid_weights(12, 4 * G, G, seed=G)
+    assert np.array_equal(oracle.fake_quant_ref(W, G), W)
+
+
 # --- exact reconstruction and the linear -------------------------------------
 
 @pytest.mark.parametrize("G,M,N,K,bias", [

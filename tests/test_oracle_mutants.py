@@ -35,6 +35,13 @@ MUTANTS = {
         "u = u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))",
         "u = u + np.uint64(0x8000)"),
     "range_min_min": ("hi = v.max(axis=2) + np.float32(0.0)", "hi = v.min(axis=2) + np.float32(1.0)"),
+    "fake_quant_drops_zero": ("w = (prod + z).astype(np.float32)", "w = prod.astype(np.float32)"),
+    "fake_quant_truncates": (
+        "    return f32_to_bf16_bits(w)\n",
+        "    return (w.view(np.uint32) >> np.uint32(16)).astype(np.uint16)\n"),
+    "fake_quant_scale_unrounded": (
+        "    s = np.repeat(bf16_bits_to_f32(s_bits), G, axis=1)\n    z = np.repeat(bf16_bits_to_f32(z_bits), G, axis=1)\n    prod",
+        "    s = np.repeat(bf16_bits_to_f32(s_bits) * np.float32(1.0 + 2.0**-9), G, axis=1)\n    z = np.repeat(bf16_bits_to_f32(z_bits), G, axis=1)\n    prod"),
 }
 
 
