@@ -32,6 +32,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # device sources each kernel is built from (a change voids its counters)
 KERNEL_SOURCES = {
     "quantize_kernel": ["quantize.hip", "w4_device.h", "w4_launch.h"],
+    "quantize_kernel_fake": ["quantize.hip", "w4_device.h", "w4_launch.h"],
     "gemv_split_kernel": ["gemv.hip", "w4_device.h", "w4_launch.h"],
     "gemm_kernel": ["gemm.hip", "w4_device.h", "w4_launch.h"],
 }
@@ -447,12 +448,12 @@ def main():
         if q_ms >= g_ms:
             b = sum(quant_bytes(N, K, G) for N, K in layers.values())
             a_gbs = b / (q_ms * 1e-3) / 1e9
-            kname = "quantize_kernel"
+            kname, klabel = "quantize_kernel", "quantize_kernel<128, false>"
             nl = len(q_ms_launch)
         else:
             b = sum(linear_bytes(1, N, K, G) for N, K in layers.values())
             a_gbs = b / (g_ms * 1e-3) / 1e9
-            kname = "gemv_split_kernel"
+            kname, klabel = "gemv_split_kernel", "gemv_split_kernel<128, 8, false>"
             nl = len(g_ms_launch)
         tr = measured_traffic(kname)
         roofline = {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,
@@ -461,12 +462,12 @@ def main():
                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                     "copy-calibrated)",
                     "traffic_detail": tr,
-                    "kernel": kname + "<128>",
+                    "kernel": klabel,
                     "avg_launch_us": round((q_ms if q_ms >= g_ms else g_ms) * 1e3 / nl, 3),
                     "bytes_per_launch_avg": b // nl}
 
-    for comp, kern in (("quantize", "quantize_kernel"), ("gemv_m1", "gemv_split_kernel"),
-                       ("gemm_m2048", "gemm_kernel")):
+    for comp, kern in (("quantize", "quantize_kernel"), ("fake_quant_g32", "quantize_kernel_fake"),
+                       ("gemv_m1", "gemv_split_kernel"), ("gemm_m2048", "gemm_kernel")):
         if comp in out:
             tr = measured_traffic(kern)
             out[comp]["traffic_bytes_per_launch"] = round(tr["bytes_per_launch"]) if tr else None
