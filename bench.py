@@ -180,7 +180,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "step", "gemv", "gemv16", "gemm", "quantize", "fake",
+    ap.add_argument("--only", choices=["all", "step", "gemv", "gemv16", "gemm", "quantize", "fake", "ps",
                                        "copy"],
                     default="all", help="restrict to one part (for profiling)")
     args = ap.parse_args()
@@ -310,24 +310,44 @@ def main():
 
     # ---- decode GEMV on its own over rotating quantized copies ----------
     g_ms_launch = {}
-    if args.only in ("all", "step", "gemv"):
+
+    def prep(c, s_, z, Gx, ps):
+        """Weights in the plain layout, or repacked to the pre-shuffled one."""
+        if not ps:
+            return c, s_, z
+        cp, sz = w4.repack_int4_preshuffled(c, s_, z, Gx)
+        return cp, sz, None
+
+    def lin(x, c, s_, z, Gx, y, ps):
+        if ps:
+            return lambda: w4.w4a16_linear_preshuffled(x, c, s_, Gx, out=y)
+        return lambda: w4.w4a16_linear(x, c, s_, z, Gx, out=y)
+
+    layouts = [False] if args.only in ("step", "gemv", "gemv16", "gemm") else \
+        [True] if args.only == "ps" else [False, True]
+    for ps in layouts:
+        sfx = "_ps" if ps else ""
+        if args.only not in ("all", "step", "gemv", "ps"):
+            break
+        if ps and args.only == "step":
+            break
         gset_bytes = sum(linear_bytes(1, N, K, G) for N, K in layers.values())
         n_g = max(2, -(-ROTATE_BYTES // gset_bytes))
-        log(f"gemv: {n_g} rotating quantized copies of {gset_bytes / 1e6:.1f} MB")
+        log(f"gemv{sfx}: {n_g} rotating quantized copies of {gset_bytes / 1e6:.1f} MB")
         gsets = []
         for r in range(n_g):
             src = sets[r % n_sets]
             entry = {}
             for name, (N, K) in layers.items():
                 W, x = src[name][0], src[name][1]
-                c, s_, z = w4.quantize_int4_grouped(W, G)
+                c, s_, z = prep(*w4.quantize_int4_grouped(W, G), G, ps)
                 entry[name] = (x, c, s_, z, torch.empty((1, N), dtype=torch.bfloat16, device=dev))
             gsets.append(entry)
         torch.cuda.synchronize()
 
         def g_fn(e, name):
             x, c, s_, z, y = e[name]
-            return lambda: w4.w4a16_linear(x, c, s_, z, G, out=y)
+            return lin(x, c, s_, z, G, y, ps)
 
         per = {}
         tot_ms = 0.0
@@ -335,7 +355,8 @@ def main():
         for name, (N, K) in layers.items():
             g = graph_of(torch, [g_fn(e, name) for e in gsets])
             ms = time_graphs(torch, [g], max(2, reps // 2)) / n_g
-            g_ms_launch[name] = ms
+            if not ps:
+                g_ms_launch[name] = ms
             b = linear_bytes(1, N, K, G)
             per[name] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1)}
             tot_ms += ms
@@ -345,8 +366,9 @@ def main():
         g = graph_of(torch, [g_fn(e, n) for e in gsets for n in names])
         set_ms = time_graphs(torch, [g], max(2, reps // 2)) / n_g
         del g
-        out["gemv_m1"] = {
-            "kernel": "gemv_split_kernel<128, 8, false>", "bound": "hbm",
+        out["gemv_m1" + sfx] = {
+            "kernel": f"gemv_split_kernel<128, 8, false, {'true' if ps else 'false'}>", "bound": "hbm",
+            "layout": "pre-shuffled" if ps else "plain",
             "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
             "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
             "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -358,11 +380,14 @@ def main():
         del gsets
 
     # ---- small-batch decode GEMV, M = 16, G = 32 (same layer shapes) ------
-    if args.only in ("all", "gemv16"):
+    for ps in layouts:
+        sfx = "_ps" if ps else ""
+        if args.only not in ("all", "gemv16", "ps"):
+            break
         M16, G16 = 16, 32
         gb16 = sum(linear_bytes(M16, N, K, G16) for N, K in layers.values())
         n16 = max(2, -(-ROTATE_BYTES // gb16))
-        log(f"gemv M=16: {n16} rotating quantized copies of {gb16 / 1e6:.1f} MB")
+        log(f"gemv M=16{sfx}: {n16} rotating quantized copies of {gb16 / 1e6:.1f} MB")
         per = {}
         tot_ms = 0.0
         tot_b = 0
@@ -370,10 +395,10 @@ def main():
             copies = []
             for r in range(n16):
                 W, x = make_layer(torch, N, K, 7000 + 100 * r + li, M16, dev)
-                c, s_, z = w4.quantize_int4_grouped(W, G16)
+                c, s_, z = prep(*w4.quantize_int4_grouped(W, G16), G16, ps)
                 del W
                 copies.append((x, c, s_, z, torch.empty((M16, N), dtype=torch.bfloat16, device=dev)))
-            fns = [(lambda e=e: w4.w4a16_linear(e[0], e[1], e[2], e[3], G16, out=e[4])) for e in copies]
+            fns = [lin(e[0], e[1], e[2], e[3], G16, e[4], ps) for e in copies]
             g = graph_of(torch, fns)
             ms = time_graphs(torch, [g], max(2, reps // 2)) / n16
             b = linear_bytes(M16, N, K, G16)
@@ -381,27 +406,33 @@ def main():
             tot_ms += ms
             tot_b += b
             del g, copies, fns
-        out["gemv_m16_g32"] = {
-            "kernel": "gemv_split_kernel<32, 8, true> (qkv, o, gate_up), gemv_direct_kernel<32, 8> (down)", "bound": "hbm",
+        t = "true" if ps else "false"
+        out["gemv_m16_g32" + sfx] = {
+            "kernel": f"gemv_split_kernel<32, 8, true, {t}> (qkv, o, gate_up), "
+                      f"gemv_direct_kernel<32, 8, {t}> (down)", "bound": "hbm",
+            "layout": "pre-shuffled" if ps else "plain",
             "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
             "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_per_set": tot_b, "per_layer": per,
         }
 
     # ---- prefill GEMM, Gemma3-12B-shaped layers, M = 2048 ----------------
-    if args.only in ("all", "gemm"):
+    for ps in layouts:
+        sfx = "_ps" if ps else ""
+        if args.only not in ("all", "gemm", "ps"):
+            break
         M = 2048
         glayers = dict(workloads.GEMMA3_12B)
-        log("gemm: Gemma3-12B-shaped layers, M=2048")
+        log(f"gemm{sfx}: Gemma3-12B-shaped layers, M=2048")
         per = {}
         tot_ms = 0.0
         tot_f = 0
         for i, (name, (N, K)) in enumerate(glayers.items()):
             W, x = make_layer(torch, N, K, 50 + i, M, dev)
-            c, s_, z = w4.quantize_int4_grouped(W, G)
+            c, s_, z = prep(*w4.quantize_int4_grouped(W, G), G, ps)
             del W
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            fn = (lambda x=x, c=c, s_=s_, z=z, y=y: w4.w4a16_linear(x, c, s_, z, G, out=y))
+            fn = lin(x, c, s_, z, G, y, ps)
             fn()
             g = graph_of(torch, [fn])
             ms = time_graphs(torch, [g], max(3, reps // 5))
@@ -410,8 +441,9 @@ def main():
             tot_ms += ms
             tot_f += f
             del g, x, c, s_, z, y
-        out["gemm_m2048"] = {
-            "kernel": "gemm_kernel<128>", "bound": "mfma",
+        out["gemm_m2048" + sfx] = {
+            "kernel": f"gemm_kernel<128, {'true' if ps else 'false'}>", "bound": "mfma",
+            "layout": "pre-shuffled" if ps else "plain",
             "avg_launch_us": round(tot_ms * 1e3 / len(glayers), 2),
             "achieved_TFLOPs": round(tot_f / (tot_ms * 1e-3) / 1e12, 1),
             "frac": round(tot_f / (tot_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -453,7 +485,7 @@ def main():
         else:
             b = sum(linear_bytes(1, N, K, G) for N, K in layers.values())
             a_gbs = b / (g_ms * 1e-3) / 1e9
-            kname, klabel = "gemv_split_kernel", "gemv_split_kernel<128, 8, false>"
+            kname, klabel = "gemv_split_kernel", "gemv_split_kernel<128, 8, false, false>"
             nl = len(g_ms_launch)
         tr = measured_traffic(kname)
         roofline = {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,

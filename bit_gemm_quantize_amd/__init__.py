@@ -16,6 +16,7 @@ from .build import LIB_PATH
 
 __all__ = [
     "W4Status", "W4Path", "W4Error", "GROUP_SIZES", "GEMV_MAX_M", "lib",
+    "repack_int4_preshuffled", "w4a16_linear_preshuffled",
     "quantize_int4_grouped", "fake_quant_int4_grouped", "w4a16_linear", "status_string",
 ]
 
@@ -68,6 +69,13 @@ def lib() -> ctypes.CDLL:
         L.w4a16_linear_select.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _i64, _i64,
                                           _p, _int, _p]
         L.w4a16_linear_select.restype = _int
+        L.repack_int4_preshuffled.argtypes = [_p, _p, _p, _i64, _i64, _i64, _p, _p, _p]
+        L.repack_int4_preshuffled.restype = _int
+        L.w4a16_linear_preshuffled.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _p]
+        L.w4a16_linear_preshuffled.restype = _int
+        L.w4a16_linear_preshuffled_select.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i64,
+                                                      _p, _int, _p]
+        L.w4a16_linear_preshuffled_select.restype = _int
         L.w4_status_string.argtypes = [_int]
         L.w4_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -180,4 +188,57 @@ def w4a16_linear(x, codes, scales, zeros, G: int, bias=None, out=None,
         int(path), _stream_ptr(x.device))
     if st != W4Status.OK:
         raise W4Error(st, "w4a16_linear")
+    return out
+
+
+def repack_int4_preshuffled(codes, scales, zeros, G: int, codes_ps=None, sz=None):
+    """Plain (codes, scales, zeros) -> pre-shuffled (codes_ps uint8 [N, K/2],
+    sz int32 [N, K/G] holding the bits s | z << 16). Outputs are allocated
+    when not given. Enqueued on torch's current stream."""
+    torch = _torch()
+    if codes.dim() != 2:
+        raise ValueError("codes must be 2-D [N, K/2]")
+    N, K = codes.shape[0], codes.shape[1] * 2
+    ng = K // G if G else 0
+    _check(codes, "codes", torch.uint8, (N, K // 2))
+    _check(scales, "scales", torch.bfloat16, (N, ng), codes.device)
+    _check(zeros, "zeros", torch.bfloat16, (N, ng), codes.device)
+    if codes_ps is None:
+        codes_ps = torch.empty((N, K // 2), dtype=torch.uint8, device=codes.device)
+    if sz is None:
+        sz = torch.empty((N, ng), dtype=torch.int32, device=codes.device)
+    _check(codes_ps, "codes_ps", torch.uint8, (N, K // 2), codes.device)
+    _check(sz, "sz", torch.int32, (N, ng), codes.device)
+    st = lib().repack_int4_preshuffled(codes.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                       N, K, G, codes_ps.data_ptr(), sz.data_ptr(),
+                                       _stream_ptr(codes.device))
+    if st != W4Status.OK:
+        raise W4Error(st, "repack_int4_preshuffled")
+    return codes_ps, sz
+
+
+def w4a16_linear_preshuffled(x, codes_ps, sz, G: int, bias=None, out=None,
+                             path: W4Path = W4Path.AUTO):
+    """w4a16_linear on the pre-shuffled layout (codes_ps, sz from
+    repack_int4_preshuffled)."""
+    torch = _torch()
+    if x.dim() != 2 or codes_ps.dim() != 2:
+        raise ValueError("x and codes_ps must be 2-D")
+    M, K = x.shape
+    N = codes_ps.shape[0]
+    ng = K // G if G else 0
+    _check(x, "x", torch.bfloat16, (M, K))
+    _check(codes_ps, "codes_ps", torch.uint8, (N, K // 2), x.device)
+    _check(sz, "sz", torch.int32, (N, ng), x.device)
+    if bias is not None:
+        _check(bias, "bias", torch.bfloat16, (N,), x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(out, "out", torch.bfloat16, (M, N), x.device)
+    st = lib().w4a16_linear_preshuffled_select(
+        x.data_ptr(), M, codes_ps.data_ptr(), sz.data_ptr(),
+        bias.data_ptr() if bias is not None else None, N, K, G, out.data_ptr(),
+        int(path), _stream_ptr(x.device))
+    if st != W4Status.OK:
+        raise W4Error(st, "w4a16_linear_preshuffled")
     return out

@@ -32,11 +32,14 @@ w4_status check_nkg(int64_t N, int64_t K, int64_t G) {
     return W4_OK;
 }
 
+// One implementation for both weight layouts: the plain one (scales and
+// zeros, sz == NULL) and the pre-shuffled one (sz, scales == zeros == NULL).
 w4_status linear_impl(const uint16_t *x, int64_t M, const uint8_t *codes,
-                      const uint16_t *scales, const uint16_t *zeros,
+                      const uint16_t *scales, const uint16_t *zeros, const uint32_t *sz,
                       const uint16_t *bias, int64_t N, int64_t K, int64_t G,
                       uint16_t *y, int path, hipStream_t stream) {
-    if (!codes || !scales || !zeros) return W4_ERR_NULL;
+    const bool pk = sz != nullptr;
+    if (!codes || (!pk && (!scales || !zeros))) return W4_ERR_NULL;
     if (M > 0 && (!x || !y)) return W4_ERR_NULL;
     if (M < 0 || M > kMaxM) return W4_ERR_SHAPE;
     const w4_status st = check_nkg(N, K, G);
@@ -45,22 +48,21 @@ w4_status linear_impl(const uint16_t *x, int64_t M, const uint8_t *codes,
     if (path != W4_PATH_AUTO && path != W4_PATH_GEMV && path != W4_PATH_GEMM)
         return W4_ERR_PATH;
     if (path == W4_PATH_GEMV && M > W4_GEMV_MAX_M) return W4_ERR_PATH;
-    if (!aligned16(codes) || !aligned16(scales) || !aligned16(zeros) ||
-        (bias && !aligned16(bias)))
-        return W4_ERR_ALIGN;
+    if (!aligned16(codes) || (bias && !aligned16(bias))) return W4_ERR_ALIGN;
+    if (pk ? !aligned16(sz) : (!aligned16(scales) || !aligned16(zeros))) return W4_ERR_ALIGN;
     if (M > 0 && (!aligned16(x) || !aligned16(y))) return W4_ERR_ALIGN;
     if (M == 0) return W4_OK;
-    const int64_t ybytes = 2 * M * N;
+    const int64_t ybytes = 2 * M * N, gbytes = 2 * N * (K / G);
     if (overlap(y, ybytes, x, 2 * M * K) || overlap(y, ybytes, codes, N * K / 2) ||
-        overlap(y, ybytes, scales, 2 * N * (K / G)) ||
-        overlap(y, ybytes, zeros, 2 * N * (K / G)) || overlap(y, ybytes, bias, 2 * N))
+        overlap(y, ybytes, scales, gbytes) || overlap(y, ybytes, zeros, gbytes) ||
+        overlap(y, ybytes, sz, 2 * gbytes) || overlap(y, ybytes, bias, 2 * N))
         return W4_ERR_ALIAS;
 
     const bool gemv = path == W4_PATH_GEMV || (path == W4_PATH_AUTO && M <= W4_GEMV_MAX_M);
     const hipError_t e =
-        gemv ? w4::launch_gemv(x, static_cast<int>(M), codes, scales, zeros, bias, N, K,
+        gemv ? w4::launch_gemv(x, static_cast<int>(M), codes, scales, zeros, sz, bias, N, K,
                                static_cast<int>(G), y, stream)
-             : w4::launch_gemm(x, M, codes, scales, zeros, bias, N, K, static_cast<int>(G),
+             : w4::launch_gemm(x, M, codes, scales, zeros, sz, bias, N, K, static_cast<int>(G),
                                y, stream);
     return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
@@ -102,14 +104,52 @@ w4_status w4a16_linear(const uint16_t *x, int64_t M, const uint8_t *codes,
                        const uint16_t *scales, const uint16_t *zeros,
                        const uint16_t *bias, int64_t N, int64_t K, int64_t G,
                        uint16_t *y, hipStream_t stream) {
-    return linear_impl(x, M, codes, scales, zeros, bias, N, K, G, y, W4_PATH_AUTO, stream);
+    return linear_impl(x, M, codes, scales, zeros, nullptr, bias, N, K, G, y, W4_PATH_AUTO,
+                       stream);
 }
 
 w4_status w4a16_linear_select(const uint16_t *x, int64_t M, const uint8_t *codes,
                               const uint16_t *scales, const uint16_t *zeros,
                               const uint16_t *bias, int64_t N, int64_t K, int64_t G,
                               uint16_t *y, int path, hipStream_t stream) {
-    return linear_impl(x, M, codes, scales, zeros, bias, N, K, G, y, path, stream);
+    return linear_impl(x, M, codes, scales, zeros, nullptr, bias, N, K, G, y, path, stream);
+}
+
+w4_status repack_int4_preshuffled(const uint8_t *codes, const uint16_t *scales,
+                                  const uint16_t *zeros, int64_t N, int64_t K, int64_t G,
+                                  uint8_t *codes_ps, uint32_t *sz, hipStream_t stream) {
+    if (!codes || !scales || !zeros || !codes_ps || !sz) return W4_ERR_NULL;
+    const w4_status st = check_nkg(N, K, G);
+    if (st != W4_OK) return st;
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(zeros) || !aligned16(codes_ps) ||
+        !aligned16(sz))
+        return W4_ERR_ALIGN;
+    const int64_t cbytes = N * K / 2, gbytes = 2 * N * (K / G);
+    const void *in[3] = {codes, scales, zeros};
+    const int64_t inb[3] = {cbytes, gbytes, gbytes};
+    for (int i = 0; i < 3; ++i)
+        if (overlap(codes_ps, cbytes, in[i], inb[i]) || overlap(sz, 2 * gbytes, in[i], inb[i]))
+            return W4_ERR_ALIAS;
+    if (overlap(codes_ps, cbytes, sz, 2 * gbytes)) return W4_ERR_ALIAS;
+    const hipError_t e = w4::launch_repack(codes, scales, zeros, N, K, static_cast<int>(G),
+                                           codes_ps, sz, stream);
+    return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
+w4_status w4a16_linear_preshuffled(const uint16_t *x, int64_t M, const uint8_t *codes_ps,
+                                   const uint32_t *sz, const uint16_t *bias, int64_t N,
+                                   int64_t K, int64_t G, uint16_t *y, hipStream_t stream) {
+    if (!sz) return W4_ERR_NULL;
+    return linear_impl(x, M, codes_ps, nullptr, nullptr, sz, bias, N, K, G, y, W4_PATH_AUTO,
+                       stream);
+}
+
+w4_status w4a16_linear_preshuffled_select(const uint16_t *x, int64_t M, const uint8_t *codes_ps,
+                                          const uint32_t *sz, const uint16_t *bias, int64_t N,
+                                          int64_t K, int64_t G, uint16_t *y, int path,
+                                          hipStream_t stream) {
+    if (!sz) return W4_ERR_NULL;
+    return linear_impl(x, M, codes_ps, nullptr, nullptr, sz, bias, N, K, G, y, path, stream);
 }
 
 const char *w4_status_string(int status) {

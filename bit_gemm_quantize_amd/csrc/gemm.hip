@@ -19,6 +19,11 @@
 //   acc += s * acc_g + (z - 128 s) * xsum_g
 // (128 + q is exact in bf16 and the MFMA accumulates exactly-representable
 // products in float32, so the only rounding is the float32 accumulation.)
+//
+// The pre-shuffled variant (PK) reads codes whose 4-byte words hold the
+// even-k nibbles in the low half and the odd-k nibbles in the high half,
+// so the expansion is a shift and one and-or per bf16 pair, and scale /
+// zero-point pairs packed in one word (one 4-byte copy per row and group).
 #include <type_traits>
 
 #include "w4_device.h"
@@ -50,15 +55,21 @@ __device__ __forceinline__ void copy2(const void *g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ushort %0, off"
                  : : "v"(g), "s"(lds) : "memory", "m0");
 }
+__device__ __forceinline__ void copy4(const void *g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 : : "v"(g), "s"(lds) : "memory", "m0");
+}
 
-template <int G>
+template <int G, bool PK>
 __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
-    const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y,
-    int64_t tile0, int64_t ntiles) {
+    const uint32_t *__restrict__ sz, const uint16_t *__restrict__ bias, int N, int K,
+    uint16_t *__restrict__ y, int64_t tile0, int64_t ntiles) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF][STAGE_BYTES];
-    constexpr int NSZ = G == 32 ? 2 : 1;         // 2-byte copies per wave and stage
+    // scale / zero-point copies per wave and stage (2 bytes each, or one
+    // 4-byte pair each in the pre-shuffled layout)
+    constexpr int NSZ = (G == 32 && !PK) ? 2 : 1;
     constexpr int Q = 4 + 1 + NSZ;               // copies per wave and stage
 
     const int tid = threadIdx.x;
@@ -109,17 +120,29 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
                    base + (wave * 4 + i) * 1024);
         // k = min(k0 + 32 * half, K - 32)
         copy16(b_src + min(k0, K - 32 - b_half * 32) / 2, base + A_BYTES + wave * 1024);
-        // scales / zero-points of the group ends in this stage: value
-        // v = 64 (NSZ w + d) + lane -> row v % 128, s|z (v / 128) % 2, end v / 256
-#pragma unroll
-        for (int d = 0; d < NSZ; ++d) {
-            const int v = 64 * (NSZ * wave + d) + lane;
-            const int row = v & 127, isz = (v >> 7) & 1, h = v >> 8;
+        if constexpr (PK) {
+            // (s | z << 16) of the group ends in this stage: value
+            // v = 64 w + lane -> row v % 128, end v / 128 (at G >= 64 both
+            // ends are the stage's one group end)
+            const int v = 64 * wave + lane;
+            const int row = v & 127, h = v >> 7;
             const int k_end = k0 + (G == 32 ? (h + 1) * 32 : KS);
             const int g = max(0, min(k_end / G - 1, ngroups - 1));
-            const uint16_t *src = (isz ? zeros : scales) +
-                                  static_cast<int64_t>(min(n0 + row, N - 1)) * ngroups + g;
-            copy2(src, base + A_BYTES + B_BYTES + 64 * 4 * (NSZ * wave + d));
+            copy4(sz + static_cast<int64_t>(min(n0 + row, N - 1)) * ngroups + g,
+                  base + A_BYTES + B_BYTES + 256 * wave);
+        } else {
+            // scales / zero-points of the group ends in this stage: value
+            // v = 64 (NSZ w + d) + lane -> row v % 128, s|z (v / 128) % 2, end v / 256
+#pragma unroll
+            for (int d = 0; d < NSZ; ++d) {
+                const int v = 64 * (NSZ * wave + d) + lane;
+                const int row = v & 127, isz = (v >> 7) & 1, h = v >> 8;
+                const int k_end = k0 + (G == 32 ? (h + 1) * 32 : KS);
+                const int g = max(0, min(k_end / G - 1, ngroups - 1));
+                const uint16_t *src = (isz ? zeros : scales) +
+                                      static_cast<int64_t>(min(n0 + row, N - 1)) * ngroups + g;
+                copy2(src, base + A_BYTES + B_BYTES + 64 * 4 * (NSZ * wave + d));
+            }
         }
     };
 
@@ -161,7 +184,10 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
             const uint32_t w = *reinterpret_cast<const uint32_t *>(
                 sb + A_BYTES + r * 32 + ((sl ^ ((r >> 3) & 1)) * 16) + kb * 4);
             uint32_t u[4];
-            unpack8_bias128(w, u, uc);
+            if constexpr (PK)
+                unpack8_bias128_il(w, u, uc);    // pre-shuffled: natural k order
+            else
+                unpack8_bias128(w, u, uc);
             b[nt] = as_bf16x8(u[0], u[1], u[2], u[3]);
         }
 #pragma unroll
@@ -183,8 +209,14 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 const int c = wn * 64 + nt * 16 + nl;
-                sv[nt] = bf16_to_f32(static_cast<uint16_t>(szp[h * 256 + c]));
-                zz[nt] = fmaf(-128.0f, sv[nt], bf16_to_f32(static_cast<uint16_t>(szp[h * 256 + 128 + c])));
+                if constexpr (PK) {
+                    const uint32_t pr = szp[h * 128 + c];
+                    sv[nt] = bf16_lo(pr);
+                    zz[nt] = fmaf(-128.0f, sv[nt], bf16_hi(pr));
+                } else {
+                    sv[nt] = bf16_to_f32(static_cast<uint16_t>(szp[h * 256 + c]));
+                    zz[nt] = fmaf(-128.0f, sv[nt], bf16_to_f32(static_cast<uint16_t>(szp[h * 256 + 128 + c])));
+                }
             }
         }
     };
@@ -245,9 +277,10 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
 } // namespace
 
 hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *codes,
-                       const uint16_t *scales, const uint16_t *zeros,
+                       const uint16_t *scales, const uint16_t *zeros, const uint32_t *sz,
                        const uint16_t *bias, int64_t N, int64_t K, int G,
                        uint16_t *y, hipStream_t stream) {
+    const bool pk = sz != nullptr;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     // one launch per 2^22 tiles keeps blocks x threads below 2^32
@@ -256,12 +289,15 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *codes,
         const int64_t nt = min(kMaxTiles, tiles - t0);
         const dim3 grid(static_cast<unsigned>(nt));
         const dim3 block(THREADS);
+#define W4_GEMM_LAUNCH(GG, PP) \
+    gemm_kernel<GG, PP><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt)
         switch (G) {
-        case 32: gemm_kernel<32><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
-        case 64: gemm_kernel<64><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
-        case 128: gemm_kernel<128><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
+        case 32: if (pk) W4_GEMM_LAUNCH(32, true); else W4_GEMM_LAUNCH(32, false); break;
+        case 64: if (pk) W4_GEMM_LAUNCH(64, true); else W4_GEMM_LAUNCH(64, false); break;
+        case 128: if (pk) W4_GEMM_LAUNCH(128, true); else W4_GEMM_LAUNCH(128, false); break;
         default: return hipErrorInvalidValue;
         }
+#undef W4_GEMM_LAUNCH
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -93,10 +93,11 @@ struct Batch {
 
 // Issue the loads of one batch: scales/zeros first (needed at the first
 // group end), then the codes. All addresses are clamped, never predicated.
-template <int G, int U>
+template <int G, int U, bool PK>
 __device__ __forceinline__ void load_batch(Batch<G, U> &b, const uint8_t *crow,
                                            const uint16_t *__restrict__ scales,
                                            const uint16_t *__restrict__ zeros,
+                                           const uint32_t *__restrict__ sz,
                                            int row0, int N, int K, int ngroups,
                                            int c, int c_last, int lane) {
     constexpr int GPC = 128 / G;
@@ -106,8 +107,13 @@ __device__ __forceinline__ void load_batch(Batch<G, U> &b, const uint8_t *crow,
     for (int r = 0; r < Batch<G, U>::R; ++r) {
         const int g = min(c * GPC + 4 * r + (lane & 3), ngroups - 1);
         const int64_t i = static_cast<int64_t>(srow) * ngroups + g;
-        b.s[r] = scales[i];
-        b.z[r] = zeros[i];
+        if constexpr (PK) {                     // one (s | z << 16) word
+            b.s[r] = sz[i];
+            b.z[r] = b.s[r] >> 16;
+        } else {
+            b.s[r] = scales[i];
+            b.z[r] = zeros[i];
+        }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -131,7 +137,7 @@ __device__ __forceinline__ uint32_t batch_sz(const uint32_t *packed, int h, int 
 // Reads past the end of a row (the padded last chunk when K % 128 != 0, or
 // groups past K / G) land in the next row or return 0; they only meet x = 0
 // and xs = 0 and add nothing.
-template <int G, int U>
+template <int G, int U, bool PK>
 __device__ __forceinline__ void load_batch_buf(Batch<G, U> &b, __amdgpu_buffer_rsrc_t crs,
                                                __amdgpu_buffer_rsrc_t srs,
                                                __amdgpu_buffer_rsrc_t zrs, int cvo, int svo,
@@ -141,8 +147,13 @@ __device__ __forceinline__ void load_batch_buf(Batch<G, U> &b, __amdgpu_buffer_r
 #pragma unroll
     for (int r = 0; r < Batch<G, U>::R; ++r) {
         const int so = (c * GPC + 4 * r) * 2;
-        b.s[r] = __builtin_amdgcn_raw_buffer_load_b16(srs, svo, so, 0);
-        b.z[r] = __builtin_amdgcn_raw_buffer_load_b16(zrs, svo, so, 0);
+        if constexpr (PK) {                     // srs covers the (s | z << 16) words
+            b.s[r] = __builtin_amdgcn_raw_buffer_load_b32(srs, 2 * svo, 2 * so, 0);
+            b.z[r] = b.s[r] >> 16;
+        } else {
+            b.s[r] = __builtin_amdgcn_raw_buffer_load_b16(srs, svo, so, 0);
+            b.z[r] = __builtin_amdgcn_raw_buffer_load_b16(zrs, svo, so, 0);
+        }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -152,11 +163,12 @@ __device__ __forceinline__ void load_batch_buf(Batch<G, U> &b, __amdgpu_buffer_r
     }
 }
 
-template <int G, int NW>
+template <int G, int NW, bool PK>
 __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
-    const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y) {
+    const uint32_t *__restrict__ sz, const uint16_t *__restrict__ bias, int N, int K,
+    uint16_t *__restrict__ y) {
     constexpr int SPG = G / 32;                 // slots per group: 4, 2 or 1
     constexpr int GPC = 128 / G;                // groups per chunk: 1, 2 or 4
     constexpr int U = G == 32 ? 2 : 4;          // chunks per batch
@@ -187,7 +199,7 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
     // Loads are unconditional (clamped addresses), so the compiler can count
     // the loads in flight and wait only for the batch being computed.
     auto load = [&](Batch<G, U> &b, int c, int c_last) {
-        load_batch<G, U>(b, crow, scales, zeros, n_base, N, K, ngroups, c, c_last, lane);
+        load_batch<G, U, PK>(b, crow, scales, zeros, sz, n_base, N, K, ngroups, c, c_last, lane);
     };
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -266,7 +278,8 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
                 if (e >= npieces) break;
                 const int m = e / per_row;
                 const int kk = (e - m * per_row) * 8;
-                *reinterpret_cast<u32x4 *>(&xl[m * kps + kk]) = interleave8_bf16(xv[j]);
+                // pre-shuffled codes expand in natural k order: x stays as is
+                *reinterpret_cast<u32x4 *>(&xl[m * kps + kk]) = PK ? xv[j] : interleave8_bf16(xv[j]);
             }
         }
         __syncthreads();
@@ -323,11 +336,12 @@ __global__ __launch_bounds__(NW * 64, 2) void gemv_phased_kernel(
 // with S = 1 each wave stores its tile directly. Lane (nl, kb) holds output
 // rows 4 kb .. 4 kb + 3 of column nl; rows >= M are computed (their A rows
 // repeat row M - 1) and never stored.
-template <int G, int S, bool NAT>
+template <int G, int S, bool NAT, bool PK>
 __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
-    const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y) {
+    const uint32_t *__restrict__ sz, const uint16_t *__restrict__ bias, int N, int K,
+    uint16_t *__restrict__ y) {
     constexpr int NW = GV_SPLIT_WAVES;
     constexpr int T = NW / S;                   // tiles per block step
     constexpr int SPG = G / 32;
@@ -389,11 +403,16 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
         const int c = cb + ld_bi * U;
         const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t *>(codes + row0 * (K >> 1)), 0, rows * (K >> 1), 0x00020000);
-        const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(scales + row0 * ngroups), 0, rows * ngroups * 2, 0x00020000);
-        const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(zeros + row0 * ngroups), 0, rows * ngroups * 2, 0x00020000);
-        load_batch_buf<G, U>(b, crs, srs, zrs, cvo, svo, c, c_last);
+        const __amdgpu_buffer_rsrc_t srs =
+            PK ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(sz + row0 * ngroups), 0,
+                                                   rows * ngroups * 4, 0x00020000)
+               : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(scales + row0 * ngroups),
+                                                   0, rows * ngroups * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t zrs =
+            PK ? srs
+               : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(zeros + row0 * ngroups),
+                                                   0, rows * ngroups * 2, 0x00020000);
+        load_batch_buf<G, U, PK>(b, crs, srs, zrs, cvo, svo, c, c_last);
         // bias of column nl (0 without bias: empty resource)
         const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(bias ? bias + row0 : bias), 0, bias ? rows * 2 : 0, 0x00020000);
@@ -427,8 +446,10 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
         }
         load_next(b0, bv0);
         load_next(b1, bv1);
-        // the copies are older than the 2 (2R + U + 1) loads of b0 and b1
-        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * (2 * R + U + 1)) : "memory");
+        // the copies are older than the loads of b0 and b1: per item R scale /
+        // zero-point words (pre-shuffled) or 2R halves, U code pieces, 1 bias
+        constexpr int LPI = (PK ? R : 2 * R) + U + 1;
+        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(2 * LPI) : "memory");
         if ((K & 127) != 0 && ce == nchunk && ce > cb) {
             // zero the pieces of the last chunk that lie past K
             const int p = lane & 15;            // logical piece in the chunk
@@ -488,7 +509,7 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
                 const int kk = k0 + p * 8;
                 const bool ok = p < seg_pr;
                 const u32x4 v = xv[j];
-                if (ok) *reinterpret_cast<u32x4 *>(&xl[m * krs + kk]) = interleave8_bf16(v);
+                if (ok) *reinterpret_cast<u32x4 *>(&xl[m * krs + kk]) = PK ? v : interleave8_bf16(v);
                 float sum = (bf16_lo(v.x) + bf16_hi(v.x)) + (bf16_lo(v.y) + bf16_hi(v.y)) +
                             (bf16_lo(v.z) + bf16_hi(v.z)) + (bf16_lo(v.w) + bf16_hi(v.w));
                 // a group's LPG pieces sit in consecutive lanes of one run
@@ -576,9 +597,9 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
             for (int j = 0; j < 4; ++j) {
                 const bool first = (j % SPG) == 0;
                 uint32_t w[4];
-                if constexpr (NAT)
+                if constexpr (NAT && !PK)
                     unpack8_bias128(b.q[u][j], w, uc);
-                else
+                else                            // interleaved x, or pre-shuffled codes
                     unpack8_bias128_il(b.q[u][j], w, uc);
                 accg = mfma16x16x32(as_bf16x8(av[j]), as_bf16x8(w[0], w[1], w[2], w[3]),
                                     first ? zero4 : accg);
@@ -655,11 +676,12 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_split_kernel(
 // lets the wait for x(t) leave codes(t + 1), codes(t + 2) in flight. Group
 // sums come from the matrix cores (fragments against ones); x and the codes
 // are expanded in natural order.
-template <int G, int S>
+template <int G, int S, bool PK>
 __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_direct_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
-    const uint16_t *__restrict__ bias, int N, int K, uint16_t *__restrict__ y) {
+    const uint32_t *__restrict__ sz, const uint16_t *__restrict__ bias, int N, int K,
+    uint16_t *__restrict__ y) {
     constexpr int NW = GV_SPLIT_WAVES;
     constexpr int T = NW / S;                   // tiles per block step
     constexpr int SPG = G / 32;
@@ -703,11 +725,16 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_direct_kernel(
         const int c = cb + ld_bi * U;
         const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t *>(codes + row0 * (K >> 1)), 0, rows * (K >> 1), 0x00020000);
-        const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(scales + row0 * ngroups), 0, rows * ngroups * 2, 0x00020000);
-        const __amdgpu_buffer_rsrc_t zrs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(zeros + row0 * ngroups), 0, rows * ngroups * 2, 0x00020000);
-        load_batch_buf<G, U>(b, crs, srs, zrs, cvo, svo, c, c_last);
+        const __amdgpu_buffer_rsrc_t srs =
+            PK ? __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t *>(sz + row0 * ngroups), 0,
+                                                   rows * ngroups * 4, 0x00020000)
+               : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(scales + row0 * ngroups),
+                                                   0, rows * ngroups * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t zrs =
+            PK ? srs
+               : __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(zeros + row0 * ngroups),
+                                                   0, rows * ngroups * 2, 0x00020000);
+        load_batch_buf<G, U, PK>(b, crs, srs, zrs, cvo, svo, c, c_last);
         const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t *>(bias ? bias + row0 : bias), 0, bias ? rows * 2 : 0, 0x00020000);
         bv = __builtin_amdgcn_raw_buffer_load_b16(brs, nl * 2, 0, 0);
@@ -778,7 +805,10 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_direct_kernel(
             for (int j = 0; j < 4; ++j) {
                 const bool first = (j % SPG) == 0;
                 uint32_t w[4];
-                unpack8_bias128(b.q[u][j], w, uc);
+                if constexpr (PK)
+                    unpack8_bias128_il(b.q[u][j], w, uc);   // natural k order
+                else
+                    unpack8_bias128(b.q[u][j], w, uc);
                 xsg = mfma16x16x32(as_bf16x8(a[u][j]), ones, first ? zero4 : xsg);
                 accg = mfma16x16x32(as_bf16x8(a[u][j]), as_bf16x8(w[0], w[1], w[2], w[3]),
                                     first ? zero4 : accg);
@@ -851,6 +881,123 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_direct_kernel(
     }
 }
 
+
+// The split kernel stages x through LDS copies (NAT) from this M on.
+constexpr int GV_NAT_MIN_M = 5;
+
+// Dynamic LDS of the split kernel for (M, K).
+size_t split_lds_bytes(int M, int K, int G) {
+    const size_t kr = static_cast<size_t>((K + 127) / 128) * 128;
+    const size_t krs = M >= GV_NAT_MIN_M ? kr : kr + GV_X_PAD;
+    return static_cast<size_t>(M) * krs * 2 + (kr / G) * GV_SPLIT_MAX_M * 4 +
+           2 * GV_SPLIT_WAVES * GV_SPLIT_MAX_M * 16 * 4;
+}
+
+template <int G, int S, bool NAT, bool PK>
+hipError_t launch_split_s(const uint16_t *x, int M, const uint8_t *codes,
+                          const uint16_t *scales, const uint16_t *zeros, const uint32_t *sz,
+                          const uint16_t *bias, int N, int K, uint16_t *y,
+                          hipStream_t stream) {
+    auto kern = gemv_split_kernel<G, S, NAT, PK>;
+    static bool attr_set[64] = {false};         // per device
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 static_cast<int>(max_lds_per_block()));
+        if (e != hipSuccess) return e;
+        if (dev >= 0 && dev < 64) attr_set[dev] = true;
+    }
+    const size_t lds = split_lds_bytes(M, K, G);
+    // resident blocks per compute unit: LDS (160 KB) and 2 blocks of 8 waves
+    int per_cu = static_cast<int>(static_cast<size_t>(GV_SPLIT_MAX_LDS) / lds);
+    per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
+    const int ntiles = (N + 15) / 16;
+    constexpr int T = GV_SPLIT_WAVES / S;
+    const int nsteps = (ntiles + T - 1) / T;
+    const int slots = compute_units() * per_cu;
+    const int blocks = nsteps < slots ? nsteps : slots;
+    kern<<<dim3(blocks), dim3(GV_SPLIT_WAVES * 64), lds, stream>>>(x, M, codes, scales, zeros,
+                                                                   sz, bias, N, K, y);
+    return hipGetLastError();
+}
+
+// K split: 8 waves per tile (measured best for the decode layers: wide
+// layers keep 8-way splits too, the persistent grid streams their tiles),
+// fewer when K has fewer than 8 chunks.
+template <int G, bool PK>
+hipError_t launch_split(const uint16_t *x, int M, const uint8_t *codes,
+                        const uint16_t *scales, const uint16_t *zeros, const uint32_t *sz,
+                        const uint16_t *bias, int N, int K, uint16_t *y,
+                        hipStream_t stream) {
+    const int nchunk = (K + 127) / 128;
+    if (M >= GV_NAT_MIN_M) {
+        if (nchunk >= 8)
+            return launch_split_s<G, 8, true, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
+        if (nchunk >= 4)
+            return launch_split_s<G, 4, true, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
+        if (nchunk >= 2)
+            return launch_split_s<G, 2, true, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
+        return launch_split_s<G, 1, true, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
+    }
+    if (nchunk >= 8)
+        return launch_split_s<G, 8, false, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
+    if (nchunk >= 4)
+        return launch_split_s<G, 4, false, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
+    if (nchunk >= 2)
+        return launch_split_s<G, 2, false, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
+    return launch_split_s<G, 1, false, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
+}
+
+template <int G, int S, bool PK>
+hipError_t launch_direct_s(const uint16_t *x, int M, const uint8_t *codes,
+                           const uint16_t *scales, const uint16_t *zeros, const uint32_t *sz,
+                           const uint16_t *bias, int N, int K, uint16_t *y,
+                           hipStream_t stream) {
+    const int ntiles = (N + 15) / 16;
+    constexpr int T = GV_SPLIT_WAVES / S;
+    const int nsteps = (ntiles + T - 1) / T;
+    const int slots = compute_units();
+    const int blocks = nsteps < slots ? nsteps : slots;
+    gemv_direct_kernel<G, S, PK><<<dim3(blocks), dim3(GV_SPLIT_WAVES * 64), 0, stream>>>(
+        x, M, codes, scales, zeros, sz, bias, N, K, y);
+    return hipGetLastError();
+}
+
+template <int G, bool PK>
+hipError_t launch_direct(const uint16_t *x, int M, const uint8_t *codes,
+                         const uint16_t *scales, const uint16_t *zeros, const uint32_t *sz,
+                         const uint16_t *bias, int N, int K, uint16_t *y,
+                         hipStream_t stream) {
+    const int nchunk = (K + 127) / 128;
+    if (nchunk >= 8)
+        return launch_direct_s<G, 8, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
+    if (nchunk >= 4)
+        return launch_direct_s<G, 4, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
+    if (nchunk >= 2)
+        return launch_direct_s<G, 2, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
+    return launch_direct_s<G, 1, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
+}
+
+template <int G, bool PK>
+hipError_t launch_gemv_g(const uint16_t *x, int M, const uint8_t *codes,
+                         const uint16_t *scales, const uint16_t *zeros, const uint32_t *sz,
+                         const uint16_t *bias, int N, int K, uint16_t *y,
+                         hipStream_t stream) {
+    const int ntiles = (N + 15) / 16;
+    if (M <= GV_SPLIT_MAX_M && split_lds_bytes(M, K, G) <= max_lds_per_block()) {
+        return launch_split<G, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
+    }
+    if (M <= GV_SPLIT_MAX_M && K % 128 == 0)
+        return launch_direct<G, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
+    gemv_phased_kernel<G, GV_WAVES, PK><<<dim3(ntiles), dim3(GV_WAVES * 64), 0, stream>>>(
+        x, M, codes, scales, zeros, sz, bias, N, K, y);
+    return hipGetLastError();
+}
+
+} // namespace
+
 int compute_units() {
     static int cus[64] = {0};
     int dev = 0;
@@ -880,133 +1027,22 @@ size_t max_lds_per_block() {
     return lds[dev];
 }
 
-// The split kernel stages x through LDS copies (NAT) from this M on.
-constexpr int GV_NAT_MIN_M = 5;
-
-// Dynamic LDS of the split kernel for (M, K).
-size_t split_lds_bytes(int M, int K, int G) {
-    const size_t kr = static_cast<size_t>((K + 127) / 128) * 128;
-    const size_t krs = M >= GV_NAT_MIN_M ? kr : kr + GV_X_PAD;
-    return static_cast<size_t>(M) * krs * 2 + (kr / G) * GV_SPLIT_MAX_M * 4 +
-           2 * GV_SPLIT_WAVES * GV_SPLIT_MAX_M * 16 * 4;
-}
-
-template <int G, int S, bool NAT>
-hipError_t launch_split_s(const uint16_t *x, int M, const uint8_t *codes,
-                          const uint16_t *scales, const uint16_t *zeros,
-                          const uint16_t *bias, int N, int K, uint16_t *y,
-                          hipStream_t stream) {
-    auto kern = gemv_split_kernel<G, S, NAT>;
-    static bool attr_set[64] = {false};         // per device
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 static_cast<int>(max_lds_per_block()));
-        if (e != hipSuccess) return e;
-        if (dev >= 0 && dev < 64) attr_set[dev] = true;
-    }
-    const size_t lds = split_lds_bytes(M, K, G);
-    // resident blocks per compute unit: LDS (160 KB) and 2 blocks of 8 waves
-    int per_cu = static_cast<int>(static_cast<size_t>(GV_SPLIT_MAX_LDS) / lds);
-    per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
-    const int ntiles = (N + 15) / 16;
-    constexpr int T = GV_SPLIT_WAVES / S;
-    const int nsteps = (ntiles + T - 1) / T;
-    const int slots = compute_units() * per_cu;
-    const int blocks = nsteps < slots ? nsteps : slots;
-    kern<<<dim3(blocks), dim3(GV_SPLIT_WAVES * 64), lds, stream>>>(x, M, codes, scales, zeros,
-                                                                   bias, N, K, y);
-    return hipGetLastError();
-}
-
-// K split: 8 waves per tile (measured best for the decode layers: wide
-// layers keep 8-way splits too, the persistent grid streams their tiles),
-// fewer when K has fewer than 8 chunks.
-template <int G>
-hipError_t launch_split(const uint16_t *x, int M, const uint8_t *codes,
-                        const uint16_t *scales, const uint16_t *zeros,
-                        const uint16_t *bias, int N, int K, uint16_t *y,
-                        hipStream_t stream) {
-    const int nchunk = (K + 127) / 128;
-    if (M >= GV_NAT_MIN_M) {
-        if (nchunk >= 8)
-            return launch_split_s<G, 8, true>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-        if (nchunk >= 4)
-            return launch_split_s<G, 4, true>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-        if (nchunk >= 2)
-            return launch_split_s<G, 2, true>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-        return launch_split_s<G, 1, true>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-    }
-    if (nchunk >= 8)
-        return launch_split_s<G, 8, false>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-    if (nchunk >= 4)
-        return launch_split_s<G, 4, false>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-    if (nchunk >= 2)
-        return launch_split_s<G, 2, false>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-    return launch_split_s<G, 1, false>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-}
-
-template <int G, int S>
-hipError_t launch_direct_s(const uint16_t *x, int M, const uint8_t *codes,
-                           const uint16_t *scales, const uint16_t *zeros,
-                           const uint16_t *bias, int N, int K, uint16_t *y,
-                           hipStream_t stream) {
-    const int ntiles = (N + 15) / 16;
-    constexpr int T = GV_SPLIT_WAVES / S;
-    const int nsteps = (ntiles + T - 1) / T;
-    const int slots = compute_units();
-    const int blocks = nsteps < slots ? nsteps : slots;
-    gemv_direct_kernel<G, S><<<dim3(blocks), dim3(GV_SPLIT_WAVES * 64), 0, stream>>>(
-        x, M, codes, scales, zeros, bias, N, K, y);
-    return hipGetLastError();
-}
-
-template <int G>
-hipError_t launch_direct(const uint16_t *x, int M, const uint8_t *codes,
-                         const uint16_t *scales, const uint16_t *zeros,
-                         const uint16_t *bias, int N, int K, uint16_t *y,
-                         hipStream_t stream) {
-    const int nchunk = (K + 127) / 128;
-    if (nchunk >= 8)
-        return launch_direct_s<G, 8>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-    if (nchunk >= 4)
-        return launch_direct_s<G, 4>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-    if (nchunk >= 2)
-        return launch_direct_s<G, 2>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-    return launch_direct_s<G, 1>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-}
-
-template <int G>
-hipError_t launch_gemv_g(const uint16_t *x, int M, const uint8_t *codes,
-                         const uint16_t *scales, const uint16_t *zeros,
-                         const uint16_t *bias, int N, int K, uint16_t *y,
-                         hipStream_t stream) {
-    const int ntiles = (N + 15) / 16;
-    if (M <= GV_SPLIT_MAX_M && split_lds_bytes(M, K, G) <= max_lds_per_block()) {
-        return launch_split<G>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-    }
-    if (M <= GV_SPLIT_MAX_M && K % 128 == 0)
-        return launch_direct<G>(x, M, codes, scales, zeros, bias, N, K, y, stream);
-    gemv_phased_kernel<G, GV_WAVES><<<dim3(ntiles), dim3(GV_WAVES * 64), 0, stream>>>(
-        x, M, codes, scales, zeros, bias, N, K, y);
-    return hipGetLastError();
-}
-
-} // namespace
-
 hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *codes,
-                       const uint16_t *scales, const uint16_t *zeros,
+                       const uint16_t *scales, const uint16_t *zeros, const uint32_t *sz,
                        const uint16_t *bias, int64_t N, int64_t K, int G,
                        uint16_t *y, hipStream_t stream) {
     const int n = static_cast<int>(N), k = static_cast<int>(K);
+    const bool pk = sz != nullptr;
+#define W4_GEMV_LAUNCH(GG) \
+    (pk ? launch_gemv_g<GG, true>(x, M, codes, scales, zeros, sz, bias, n, k, y, stream) \
+        : launch_gemv_g<GG, false>(x, M, codes, scales, zeros, sz, bias, n, k, y, stream))
     switch (G) {
-    case 32: return launch_gemv_g<32>(x, M, codes, scales, zeros, bias, n, k, y, stream);
-    case 64: return launch_gemv_g<64>(x, M, codes, scales, zeros, bias, n, k, y, stream);
-    case 128: return launch_gemv_g<128>(x, M, codes, scales, zeros, bias, n, k, y, stream);
+    case 32: return W4_GEMV_LAUNCH(32);
+    case 64: return W4_GEMV_LAUNCH(64);
+    case 128: return W4_GEMV_LAUNCH(128);
     default: return hipErrorInvalidValue;
     }
+#undef W4_GEMV_LAUNCH
 }
 
 } // namespace w4

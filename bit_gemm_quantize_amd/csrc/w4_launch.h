@@ -7,6 +7,11 @@
 
 namespace w4 {
 
+// Compute units of the current device, and the LDS one workgroup may use
+// (at most 160 KB), cached per device.
+int compute_units();
+size_t max_lds_per_block();
+
 hipError_t launch_quantize(const uint16_t *W, int64_t N, int64_t K, int G,
                            uint8_t *codes, uint16_t *scales, uint16_t *zeros,
                            hipStream_t stream);
@@ -15,15 +20,21 @@ hipError_t launch_quantize(const uint16_t *W, int64_t N, int64_t K, int G,
 hipError_t launch_fake_quant(const uint16_t *W, int64_t N, int64_t K, int G, uint16_t *what,
                              hipStream_t stream);
 
-// Decode GEMV, 1 <= M <= 16.
+// Plain layout -> pre-shuffled layout (codes_ps [N, K/2], sz [N, K/G]).
+hipError_t launch_repack(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros,
+                         int64_t N, int64_t K, int G, uint8_t *codes_ps, uint32_t *sz,
+                         hipStream_t stream);
+
+// Decode GEMV, 1 <= M <= 16. Plain layout (scales, zeros; sz == NULL) or
+// pre-shuffled layout (codes pre-shuffled, sz != NULL; scales, zeros unused).
 hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *codes,
-                       const uint16_t *scales, const uint16_t *zeros,
+                       const uint16_t *scales, const uint16_t *zeros, const uint32_t *sz,
                        const uint16_t *bias, int64_t N, int64_t K, int G,
                        uint16_t *y, hipStream_t stream);
 
-// Prefill GEMM, any M >= 1.
+// Prefill GEMM, any M >= 1; layouts as launch_gemv.
 hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *codes,
-                       const uint16_t *scales, const uint16_t *zeros,
+                       const uint16_t *scales, const uint16_t *zeros, const uint32_t *sz,
                        const uint16_t *bias, int64_t N, int64_t K, int G,
                        uint16_t *y, hipStream_t stream);
 

@@ -157,6 +157,50 @@ w4_status w4a16_linear_select(const uint16_t *x, int64_t M,
                               int64_t N, int64_t K, int64_t G, uint16_t *y,
                               int path, hipStream_t stream);
 
+/*
+ * Pre-shuffled weight layout. The pages' int4 paths ship kernel-specific
+ * packings beside the plain one (torchao README ("PyTorch原生训练至推理模型优化"),
+ * int4 weight quantization: the weight-only config takes a packing format,
+ * tile-packed for one accelerator and plain for another; torchao release
+ * notes, "New Features": a pre-shuffled int4 tensor). They give no format;
+ * this one is the library's own, made for its gfx950 kernels. The plain
+ * layout stays the interchange format; the pre-shuffled one holds the same
+ * q, s and z and gives the same results.
+ *
+ *   codes_ps [N, K/2] bytes: each 4-byte word (little endian) holds the
+ *            codes of k = 8j .. 8j+7 of its row with nibble i = q[8j + 2i]
+ *            and nibble 4 + i = q[8j + 2i + 1], i = 0..3 (even k in the low
+ *            half-word, odd k in the high one)
+ *   sz       uint32 [N, K/G]: s[n][g] | z[n][g] << 16 (bf16 bits)
+ *
+ * repack_int4_preshuffled - plain (codes, scales, zeros) -> (codes_ps, sz).
+ * A pure rearrangement: bit-exact and deterministic.
+ *
+ * codes, scales, zeros   in   as produced by quantize_int4_grouped
+ * N, K, G  in   as for quantize_int4_grouped
+ * codes_ps out  [N, K/2] bytes; sz out uint32 [N, K/G]; no overlap with the
+ *               inputs or each other (W4_ERR_ALIAS)
+ */
+w4_status repack_int4_preshuffled(const uint8_t *codes, const uint16_t *scales,
+                                  const uint16_t *zeros, int64_t N, int64_t K, int64_t G,
+                                  uint8_t *codes_ps, uint32_t *sz, hipStream_t stream);
+
+/*
+ * w4a16_linear_preshuffled - w4a16_linear on the pre-shuffled layout: same
+ * arguments (codes_ps and sz in place of codes, scales and zeros), same
+ * validation and status codes, the same result to float32 accumulation
+ * error. sz must be 16-byte aligned.
+ */
+w4_status w4a16_linear_preshuffled(const uint16_t *x, int64_t M, const uint8_t *codes_ps,
+                                   const uint32_t *sz, const uint16_t *bias, int64_t N,
+                                   int64_t K, int64_t G, uint16_t *y, hipStream_t stream);
+
+/* w4a16_linear_preshuffled with an explicit kernel path, as w4a16_linear_select. */
+w4_status w4a16_linear_preshuffled_select(const uint16_t *x, int64_t M, const uint8_t *codes_ps,
+                                          const uint32_t *sz, const uint16_t *bias, int64_t N,
+                                          int64_t K, int64_t G, uint16_t *y, int path,
+                                          hipStream_t stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *w4_status_string(int status);
 

@@ -1,5 +1,6 @@
 """CPU oracle for group-wise asymmetric int4 weight-only quantization, its
-fake-quantize round trip, and the W4A16 linear layer.
+fake-quantize round trip, the pre-shuffled weight layout, and the W4A16
+linear layer.
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
 execute this package: only the test suite, the smoke check and the CPU
@@ -12,6 +13,7 @@ from .ref import (  # noqa: F401
     f32_to_bf16_bits,
     quantize_ref,
     unpack_codes_ref,
+    repack_preshuffled_ref,
     dequant_ref,
     fake_quant_ref,
     linear_ref,

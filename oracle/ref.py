@@ -28,6 +28,10 @@ Sources (web pages; cited by title and section):
     step; "torchao模型量化完全指南" section 4.1: QAT simulates the
     quantization error during training; the torchao release notes page,
     "BC Breaking": the int4 weight fake-quantize config.
+  * torchao README, int4 weight quantization example: the weight-only config
+    takes a packing format (a tile-packed one for one accelerator, a plain
+    one for another); torchao release notes, "New Features": a pre-shuffled
+    int4 tensor. No format is given (R17).
 
 Readings taken where the pages leave the step open (each is listed in the
 design notes of the repository):
@@ -55,6 +59,11 @@ design notes of the repository):
       uses) returns bf16_rne( fl32( q * s + z ) ) per element, with q, s, z
       exactly as the quantizer computes them: the dequantization in binary32
       like every other step, then rounded to the bf16 weight dtype.
+  R17 pre-shuffled layout: the pages name kernel-specific int4 packings but
+      give none; the library's own is a rearrangement of the plain format:
+      each 4-byte word (little endian) of a row holds the codes of 8
+      consecutive k = 8j .. 8j+7 with nibble i = q[8j + 2i] and nibble
+      4 + i = q[8j + 2i + 1] (i = 0..3), and sz[n, g] = s | z << 16.
 """
 from __future__ import annotations
 
@@ -159,6 +168,27 @@ def unpack_codes_ref(codes: np.ndarray) -> np.ndarray:
     q[:, 0::2] = codes & np.uint8(0x0F)
     q[:, 1::2] = codes >> np.uint8(4)
     return q
+
+
+def repack_preshuffled_ref(codes, scales_bits, zeros_bits, G: int):
+    """Plain layout -> pre-shuffled layout (R17), by code index.
+
+    Returns (codes_ps uint8 [N, K/2], sz uint32 [N, K/G]). Every word's eight
+    codes are listed by nibble position: the four even-k codes, then the
+    four odd-k codes; nibble positions 2b and 2b + 1 fill byte b (low, high).
+    """
+    q = unpack_codes_ref(codes)
+    N, K = q.shape
+    _check_group(K, G)
+    words = q.reshape(N, K // 8, 8)
+    nib = np.concatenate([words[:, :, 0::2], words[:, :, 1::2]], axis=2)   # positions 0..7
+    b = (nib[:, :, 0::2] | (nib[:, :, 1::2] << np.uint8(4))).astype(np.uint8)
+    codes_ps = b.reshape(N, K // 2)
+    s = np.asarray(scales_bits, dtype=np.uint16).astype(np.uint32)
+    z = np.asarray(zeros_bits, dtype=np.uint16).astype(np.uint32)
+    if s.shape != (N, K // G) or z.shape != (N, K // G):
+        raise ValueError("scales/zeros must be [N, K/G]")
+    return codes_ps, (s | (z << np.uint32(16))).astype(np.uint32)
 
 
 def dequant_ref(codes, scales_bits, zeros_bits, G: int) -> np.ndarray:

@@ -48,19 +48,16 @@ class Guarded:
     def __init__(self, shape, dtype):
         esz = torch.empty((), dtype=dtype).element_size()
         n = int(np.prod(shape))
-        g = GUARD // esz
-        self.buf = torch.full((n + 2 * g,), 0, dtype=torch.uint8 if esz == 1 else torch.int16,
-                              device="cuda")
-        self.buf.view(torch.uint8).fill_(FILL)
-        self.g = g
-        self.n = n
-        self.tensor = self.buf[g:g + n].view(dtype).view(*shape)
+        # one byte buffer; the tensor starts GUARD bytes in (a multiple of
+        # every element size, so the view stays aligned)
+        self.buf = torch.full((n * esz + 2 * GUARD,), FILL, dtype=torch.uint8, device="cuda")
+        self.nbytes = n * esz
+        self.tensor = self.buf[GUARD:GUARD + n * esz].view(dtype).view(*shape)
 
     def check_guards(self):
-        raw = self.buf.view(torch.uint8).cpu().numpy()
-        esz = self.buf.element_size()
-        lo = raw[: self.g * esz]
-        hi = raw[(self.g + self.n) * esz:]
+        raw = self.buf.cpu().numpy()
+        lo = raw[:GUARD]
+        hi = raw[GUARD + self.nbytes:]
         assert np.all(lo == FILL) and np.all(hi == FILL), "write outside the output"
 
 

@@ -251,6 +251,43 @@ def check_fake_quant(fake_quant, quantize, W_bits, G):
     assert np.array_equal(got[cmask], w[cmask] + 0.0), "constant group changed"
 
 
+def check_preshuffle(repack, W_codes_seed=17):
+    """The pre-shuffled layout (R17), pinned three ways that do not share the
+    oracle's index arithmetic:
+      * a word worked out by hand: codes k = 0..7 equal to 0..7 give the
+        bytes 0x20, 0x64, 0x31, 0x75 (nibbles 0, 2, 4, 6 | 1, 3, 5, 7), and
+        sz holds s in the low and z in the high half-word;
+      * its purpose: for every word and i = 0..3, ((w >> 4i) & 0x000F000F) |
+        0x43004300 read as two bf16 values is (128 + q[8j+2i], 128 +
+        q[8j+2i+1]) with q read from the plain codes;
+      * it is a rearrangement: per row the multiset of nibbles is unchanged."""
+    q = np.tile(np.arange(8, dtype=np.uint8), 4).reshape(1, 32)
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    cp, sz = repack(codes, np.array([[0x3F80]], np.uint16), np.array([[0xBF80]], np.uint16), 32)
+    assert cp.dtype == np.uint8 and cp.shape == (1, 16)
+    assert list(cp[0, :4]) == [0x20, 0x64, 0x31, 0x75], [hex(v) for v in cp[0, :4]]
+    assert sz.dtype == np.uint32 and int(sz[0, 0]) == 0xBF803F80
+    rng = np.random.default_rng(W_codes_seed)
+    for (N, K, G) in ((3, 64, 32), (2, 256, 128), (5, 128, 64)):
+        codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        s_bits = rng.integers(0, 1 << 16, (N, K // G), dtype=np.uint16)
+        z_bits = rng.integers(0, 1 << 16, (N, K // G), dtype=np.uint16)
+        cp, sz = repack(codes, s_bits, z_bits, G)
+        qq = unpack_test(codes).astype(np.uint32)
+        words = cp.view("<u4")                      # [N, K / 8]
+        for i in range(4):
+            pair = ((words >> np.uint32(4 * i)) & np.uint32(0x000F000F)) | np.uint32(0x43004300)
+            lo = f32_from_bf16((pair & 0xFFFF).astype(np.uint16))
+            hi = f32_from_bf16((pair >> 16).astype(np.uint16))
+            assert np.array_equal(lo, 128.0 + qq[:, 2 * i::8]), f"pair {i} low"
+            assert np.array_equal(hi, 128.0 + qq[:, 2 * i + 1::8]), f"pair {i} high"
+        for n in range(N):
+            a = np.sort(np.r_[cp[n] & 15, cp[n] >> 4])
+            b = np.sort(np.r_[codes[n] & 15, codes[n] >> 4])
+            assert np.array_equal(a, b), "not a rearrangement"
+        assert np.array_equal(sz & 0xFFFF, s_bits) and np.array_equal(sz >> 16, z_bits)
+
+
 def run_all_pins(mod):
     """Every pin against an oracle module-like object."""
     check_bf16_helper(mod.f32_to_bf16_bits)
@@ -269,3 +306,5 @@ def run_all_pins(mod):
         V = rng.standard_normal((8, 256)) * 10.0 ** rng.integers(-3, 3, (8, 1))
         V[2, :32] = -1.5
         check_fake_quant(mod.fake_quant_ref, mod.quantize_ref, bf16_from_float(V), 32)
+    if hasattr(mod, "repack_preshuffled_ref"):
+        check_preshuffle(mod.repack_preshuffled_ref)

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
         "quantize_int4_grouped", "fake_quant_int4_grouped", "w4a16_linear",
-        "w4a16_linear_select", "w4_status_string"])
+        "w4a16_linear_select", "repack_int4_preshuffled", "w4a16_linear_preshuffled",
+        "w4a16_linear_preshuffled_select", "w4_status_string"])
 
 
 def test_library_exports_every_declared_function(L):
@@ -141,6 +142,54 @@ def test_linear_validation(L, kw, expect):
 def test_linear_plain_entry_point_validates(L):
     assert L.w4a16_linear(A, 1, None, C, D, None, 64, 128, 32, E, None) == w4.W4Status.ERR_NULL
     assert L.w4a16_linear(A, 0, B, C, D, None, 64, 128, 32, E, None) == w4.W4Status.OK
+
+
+def rp(L, codes=A, s=B, z=C, N=64, K=128, G=32, out=D, sz=E):
+    return L.repack_int4_preshuffled(codes, s, z, N, K, G, out, sz, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(codes=None), w4.W4Status.ERR_NULL),
+    (dict(sz=None), w4.W4Status.ERR_NULL),
+    (dict(z=None), w4.W4Status.ERR_NULL),
+    (dict(N=0), w4.W4Status.ERR_SHAPE),
+    (dict(K=96, G=64), w4.W4Status.ERR_SHAPE),
+    (dict(G=8), w4.W4Status.ERR_GROUP),
+    (dict(out=D + 4), w4.W4Status.ERR_ALIGN),
+    (dict(sz=E + 8), w4.W4Status.ERR_ALIGN),
+    (dict(out=A), w4.W4Status.ERR_ALIAS),                    # in place
+    (dict(sz=B + 16), w4.W4Status.ERR_ALIAS),                # sz over the scales
+    (dict(sz=D + 16), w4.W4Status.ERR_ALIAS),                # sz inside codes_ps
+])
+def test_repack_validation(L, kw, expect):
+    assert rp(L, **kw) == expect
+
+
+def lin_ps(L, x=A, M=4, codes=B, sz=C, bias=None, N=64, K=128, G=32, y=E, path=0):
+    return L.w4a16_linear_preshuffled_select(x, M, codes, sz, bias, N, K, G, y, path, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(codes=None), w4.W4Status.ERR_NULL),
+    (dict(sz=None), w4.W4Status.ERR_NULL),
+    (dict(x=None), w4.W4Status.ERR_NULL),
+    (dict(M=-1), w4.W4Status.ERR_SHAPE),
+    (dict(K=48, G=32), w4.W4Status.ERR_SHAPE),
+    (dict(G=100), w4.W4Status.ERR_GROUP),
+    (dict(path=3), w4.W4Status.ERR_PATH),
+    (dict(path=1, M=17), w4.W4Status.ERR_PATH),
+    (dict(sz=C + 4), w4.W4Status.ERR_ALIGN),
+    (dict(y=C), w4.W4Status.ERR_ALIAS),                      # y over sz
+    (dict(M=0, x=None, y=None), w4.W4Status.OK),
+])
+def test_linear_preshuffled_validation(L, kw, expect):
+    assert lin_ps(L, **kw) == expect
+
+
+def test_linear_preshuffled_auto_entry_point_validates(L):
+    assert L.w4a16_linear_preshuffled(A, 1, B, None, None, 64, 128, 32, E, None) == \
+        w4.W4Status.ERR_NULL
+    assert L.w4a16_linear_preshuffled(A, 0, B, C, None, 64, 128, 32, E, None) == w4.W4Status.OK
 
 
 def test_binding_rejects_host_tensors():

@@ -42,6 +42,18 @@ MUTANTS = {
     "fake_quant_scale_unrounded": (
         "    s = np.repeat(bf16_bits_to_f32(s_bits), G, axis=1)\n    z = np.repeat(bf16_bits_to_f32(z_bits), G, axis=1)\n    prod",
         "    s = np.repeat(bf16_bits_to_f32(s_bits) * np.float32(1.0 + 2.0**-9), G, axis=1)\n    z = np.repeat(bf16_bits_to_f32(z_bits), G, axis=1)\n    prod"),
+    "preshuffle_odd_first": (
+        "nib = np.concatenate([words[:, :, 0::2], words[:, :, 1::2]], axis=2)",
+        "nib = np.concatenate([words[:, :, 1::2], words[:, :, 0::2]], axis=2)"),
+    "preshuffle_bytes_high_first": (
+        "b = (nib[:, :, 0::2] | (nib[:, :, 1::2] << np.uint8(4))).astype(np.uint8)",
+        "b = (nib[:, :, 1::2] | (nib[:, :, 0::2] << np.uint8(4))).astype(np.uint8)"),
+    "preshuffle_natural_nibbles": (
+        "nib = np.concatenate([words[:, :, 0::2], words[:, :, 1::2]], axis=2)",
+        "nib = words"),
+    "preshuffle_sz_swapped": (
+        "return codes_ps, (s | (z << np.uint32(16))).astype(np.uint32)",
+        "return codes_ps, (z | (s << np.uint32(16))).astype(np.uint32)"),
 }
 
 
