@@ -35,6 +35,7 @@ KERNEL_SOURCES = {
     "quantize_kernel_fake": ["quantize.hip", "w4_device.h", "w4_launch.h"],
     "gemv_split_kernel": ["gemv.hip", "w4_device.h", "w4_launch.h"],
     "gemm_kernel": ["gemm.hip", "w4_device.h", "w4_launch.h"],
+    "gemm_kernel_ps": ["gemm.hip", "w4_device.h", "w4_launch.h"],
 }
 
 
@@ -499,7 +500,8 @@ def main():
                     "bytes_per_launch_avg": b // nl}
 
     for comp, kern in (("quantize", "quantize_kernel"), ("fake_quant_g32", "quantize_kernel_fake"),
-                       ("gemv_m1", "gemv_split_kernel"), ("gemm_m2048", "gemm_kernel")):
+                       ("gemv_m1", "gemv_split_kernel"), ("gemm_m2048", "gemm_kernel"),
+                       ("gemm_m2048_ps", "gemm_kernel_ps")):
         if comp in out:
             tr = measured_traffic(kern)
             out[comp]["traffic_bytes_per_launch"] = round(tr["bytes_per_launch"]) if tr else None
