@@ -26,6 +26,7 @@ METRIC = ("W4A16 linear: achieved HBM GB/s (M=1) and TFLOP/s (M=2048), "
           "% of roofline")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
+MFMA_INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 matrix peak
 ROTATE_BYTES = 1 << 30          # rotate weight copies over >= 1 GiB
 CSRC = os.path.join(ROOT, "bit_gemm_quantize_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -181,7 +182,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "step", "gemv", "gemv16", "gemm", "quantize", "fake", "ps",
+    ap.add_argument("--only", choices=["all", "step", "gemv", "gemv16", "gemm", "quantize", "fake", "ps", "w4a8",
                                        "copy"],
                     default="all", help="restrict to one part (for profiling)")
     args = ap.parse_args()
@@ -452,6 +453,49 @@ def main():
             "per_layer": per,
             "set_us": round(tot_ms * 1e3, 2),
         }
+
+    # ---- W4A8: per-token int8 activations + int4 weights on int8 MFMA -----
+    if args.only in ("all", "w4a8"):
+        M = 2048
+        glayers = dict(workloads.GEMMA3_12B)
+        for Gw in (128, 32):
+            log(f"w4a8 G={Gw}: Gemma3-12B-shaped layers, M=2048")
+            per = {}
+            tot_ms = tot_aq_ms = 0.0
+            tot_f = tot_aq_b = 0
+            for i, (name, (N, K)) in enumerate(glayers.items()):
+                W, x = make_layer(torch, N, K, 50 + i, M, dev)
+                c, s_, z = w4.quantize_int4_grouped(W, Gw)
+                del W
+                x8, sx = w4.quantize_act_int8(x)
+                y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+                fn = (lambda x8=x8, sx=sx, c=c, s_=s_, z=z, y=y, Gw=Gw:
+                      w4.w4a8_linear(x8, sx, c, s_, z, Gw, out=y))
+                fn()
+                g = graph_of(torch, [fn])
+                ms = time_graphs(torch, [g], max(3, reps // 5))
+                del g
+                aq = (lambda x=x, x8=x8, sx=sx: w4.quantize_act_int8(x, x8=x8, sx=sx))
+                g = graph_of(torch, [aq])
+                ms_aq = time_graphs(torch, [g], max(3, reps // 5))
+                del g
+                f = 2 * M * N * K
+                per[name] = {"us": round(ms * 1e3, 2), "TOPs": round(f / (ms * 1e-3) / 1e12, 1),
+                             "act_quant_us": round(ms_aq * 1e3, 2)}
+                tot_ms += ms
+                tot_f += f
+                tot_aq_ms += ms_aq
+                tot_aq_b += 3 * M * K + 4 * M
+                del x, x8, sx, c, s_, z, y
+            out[f"w4a8_gemm_m2048_g{Gw}"] = {
+                "kernel": f"w4a8_gemm_kernel<{Gw}>", "bound": "mfma (int8)",
+                "achieved_TOPs": round(tot_f / (tot_ms * 1e-3) / 1e12, 1),
+                "frac": round(tot_f / (tot_ms * 1e-3) / 1e12 / MFMA_INT8_PEAK_TOPS, 4),
+                "ops_per_set": tot_f, "set_us": round(tot_ms * 1e3, 2), "per_layer": per,
+                "act_quant": {"kernel": "act_quant_kernel", "bound": "hbm",
+                              "achieved_GBps": round(tot_aq_b / (tot_aq_ms * 1e-3) / 1e9, 1),
+                              "set_us": round(tot_aq_ms * 1e3, 2)},
+            }
 
     # ---- achievable-bandwidth reference: torch's own device copy ----------
     # The same buffers calibrate the HBM byte counters: an elementwise

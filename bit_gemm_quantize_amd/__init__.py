@@ -16,7 +16,7 @@ from .build import LIB_PATH
 
 __all__ = [
     "W4Status", "W4Path", "W4Error", "GROUP_SIZES", "GEMV_MAX_M", "lib",
-    "repack_int4_preshuffled", "w4a16_linear_preshuffled",
+    "repack_int4_preshuffled", "w4a16_linear_preshuffled", "quantize_act_int8", "w4a8_linear",
     "quantize_int4_grouped", "fake_quant_int4_grouped", "w4a16_linear", "status_string",
 ]
 
@@ -76,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.w4a16_linear_preshuffled_select.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i64,
                                                       _p, _int, _p]
         L.w4a16_linear_preshuffled_select.restype = _int
+        L.quantize_act_int8.argtypes = [_p, _i64, _i64, _p, _p, _p]
+        L.quantize_act_int8.restype = _int
+        L.w4a8_linear.argtypes = [_p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p]
+        L.w4a8_linear.restype = _int
         L.w4_status_string.argtypes = [_int]
         L.w4_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -241,4 +245,53 @@ def w4a16_linear_preshuffled(x, codes_ps, sz, G: int, bias=None, out=None,
         int(path), _stream_ptr(x.device))
     if st != W4Status.OK:
         raise W4Error(st, "w4a16_linear_preshuffled")
+    return out
+
+
+def quantize_act_int8(x, x8=None, sx=None):
+    """Per-token symmetric int8 of a bf16 GPU x[M, K] (K a multiple of 32).
+    Returns (x8 int8 [M, K], sx float32 [M])."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    M, K = x.shape
+    _check(x, "x", torch.bfloat16, (M, K))
+    if x8 is None:
+        x8 = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if sx is None:
+        sx = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check(x8, "x8", torch.int8, (M, K), x.device)
+    _check(sx, "sx", torch.float32, (M,), x.device)
+    st = lib().quantize_act_int8(x.data_ptr(), M, K, x8.data_ptr(), sx.data_ptr(),
+                                 _stream_ptr(x.device))
+    if st != W4Status.OK:
+        raise W4Error(st, "quantize_act_int8")
+    return x8, sx
+
+
+def w4a8_linear(x8, sx, codes, scales, zeros, G: int, bias=None, out=None):
+    """W4A8 linear: int8 activations (quantize_act_int8) with the int4
+    weights of quantize_int4_grouped; y bf16 [M, N]."""
+    torch = _torch()
+    if x8.dim() != 2 or codes.dim() != 2:
+        raise ValueError("x8 and codes must be 2-D")
+    M, K = x8.shape
+    N = codes.shape[0]
+    ng = K // G if G else 0
+    _check(x8, "x8", torch.int8, (M, K))
+    _check(sx, "sx", torch.float32, (M,), x8.device)
+    _check(codes, "codes", torch.uint8, (N, K // 2), x8.device)
+    _check(scales, "scales", torch.bfloat16, (N, ng), x8.device)
+    _check(zeros, "zeros", torch.bfloat16, (N, ng), x8.device)
+    if bias is not None:
+        _check(bias, "bias", torch.bfloat16, (N,), x8.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x8.device)
+    _check(out, "out", torch.bfloat16, (M, N), x8.device)
+    st = lib().w4a8_linear(x8.data_ptr(), sx.data_ptr(), M, codes.data_ptr(),
+                           scales.data_ptr(), zeros.data_ptr(),
+                           bias.data_ptr() if bias is not None else None, N, K, G,
+                           out.data_ptr(), _stream_ptr(x8.device))
+    if st != W4Status.OK:
+        raise W4Error(st, "w4a8_linear")
     return out

@@ -152,6 +152,44 @@ w4_status w4a16_linear_preshuffled_select(const uint16_t *x, int64_t M, const ui
     return linear_impl(x, M, codes_ps, nullptr, nullptr, sz, bias, N, K, G, y, path, stream);
 }
 
+w4_status quantize_act_int8(const uint16_t *x, int64_t M, int64_t K, int8_t *x8, float *sx,
+                            hipStream_t stream) {
+    if (M < 0 || M > kMaxM || K < 32 || K > kMaxDim || K % 32 != 0 || M * K > kMaxElems)
+        return W4_ERR_SHAPE;
+    if (M == 0) return W4_OK;
+    if (!x || !x8 || !sx) return W4_ERR_NULL;
+    if (!aligned16(x) || !aligned16(x8) || !aligned16(sx)) return W4_ERR_ALIGN;
+    if (overlap(x8, M * K, x, 2 * M * K) || overlap(sx, 4 * M, x, 2 * M * K) ||
+        overlap(sx, 4 * M, x8, M * K))
+        return W4_ERR_ALIAS;
+    const hipError_t e = w4::launch_act_quant(x, M, K, x8, sx, stream);
+    return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
+w4_status w4a8_linear(const int8_t *x8, const float *sx, int64_t M, const uint8_t *codes,
+                      const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
+                      int64_t N, int64_t K, int64_t G, uint16_t *y, hipStream_t stream) {
+    if (!codes || !scales || !zeros) return W4_ERR_NULL;
+    if (M > 0 && (!x8 || !sx || !y)) return W4_ERR_NULL;
+    if (M < 0 || M > kMaxM) return W4_ERR_SHAPE;
+    const w4_status st = check_nkg(N, K, G);
+    if (st != W4_OK) return st;
+    if (K % 64 != 0 || M * K > kMaxElems || M * N > kMaxElems) return W4_ERR_SHAPE;
+    if (!aligned16(codes) || !aligned16(scales) || !aligned16(zeros) ||
+        (bias && !aligned16(bias)))
+        return W4_ERR_ALIGN;
+    if (M > 0 && (!aligned16(x8) || !aligned16(sx) || !aligned16(y))) return W4_ERR_ALIGN;
+    if (M == 0) return W4_OK;
+    const int64_t ybytes = 2 * M * N, gbytes = 2 * N * (K / G);
+    if (overlap(y, ybytes, x8, M * K) || overlap(y, ybytes, sx, 4 * M) ||
+        overlap(y, ybytes, codes, N * K / 2) || overlap(y, ybytes, scales, gbytes) ||
+        overlap(y, ybytes, zeros, gbytes) || overlap(y, ybytes, bias, 2 * N))
+        return W4_ERR_ALIAS;
+    const hipError_t e = w4::launch_w4a8_gemm(x8, sx, M, codes, scales, zeros, bias, N, K,
+                                              static_cast<int>(G), y, stream);
+    return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
 const char *w4_status_string(int status) {
     switch (status) {
     case W4_OK: return "W4_OK: success";

@@ -25,6 +25,16 @@ hipError_t launch_repack(const uint8_t *codes, const uint16_t *scales, const uin
                          int64_t N, int64_t K, int G, uint8_t *codes_ps, uint32_t *sz,
                          hipStream_t stream);
 
+// Per-token int8 activations: x8 [M, K], sx [M].
+hipError_t launch_act_quant(const uint16_t *x, int64_t M, int64_t K, int8_t *x8, float *sx,
+                            hipStream_t stream);
+
+// W4A8 linear on the int8 matrix cores, any M >= 1, K % 64 == 0.
+hipError_t launch_w4a8_gemm(const int8_t *x8, const float *sx, int64_t M, const uint8_t *codes,
+                            const uint16_t *scales, const uint16_t *zeros,
+                            const uint16_t *bias, int64_t N, int64_t K, int G, uint16_t *y,
+                            hipStream_t stream);
+
 // Decode GEMV, 1 <= M <= 16. Plain layout (scales, zeros; sz == NULL) or
 // pre-shuffled layout (codes pre-shuffled, sz != NULL; scales, zeros unused).
 hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *codes,

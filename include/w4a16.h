@@ -201,6 +201,42 @@ w4_status w4a16_linear_preshuffled_select(const uint16_t *x, int64_t M, const ui
                                           int64_t K, int64_t G, uint16_t *y, int path,
                                           hipStream_t stream);
 
+/*
+ * W4A8: int8 activations with the int4 weights above, on the int8 matrix
+ * cores (torchao README ("PyTorch原生训练至推理模型优化"): int8 dynamic
+ * activations with group-wise int4 weights, the edge and QAT configuration,
+ * group size 32 in its example; "Optimum Quanto", "Design overview /
+ * Tensors": int8 takes a symmetric projection per tensor or per channel;
+ * the per-token reading is this library's, stated in its design notes).
+ *
+ * quantize_act_int8 - per-token (per row) symmetric int8 of x:
+ *   a = max_k |x[m][k]|;  sx[m] = fl32(a / 127);
+ *   x8[m][k] = clamp(rne(fl32(x[m][k] / sx[m])), -127, 127), 0 where a == 0
+ * (IEEE binary32 division, ties to even). Bit-exact and deterministic.
+ *
+ * x   in   bf16 [M, K]; M >= 0 (0: nothing is launched, pointers may be
+ *          NULL), K a multiple of 32
+ * x8  out  int8 [M, K] (natural k order); sx out float32 [M]; neither may
+ *          overlap x or the other
+ */
+w4_status quantize_act_int8(const uint16_t *x, int64_t M, int64_t K, int8_t *x8, float *sx,
+                            hipStream_t stream);
+
+/*
+ * w4a8_linear - y = sx[m] * sum_g ( s[n][g] * P + z[n][g] * X ) (+ bias[n]),
+ * P = sum_{k in g} x8[m][k] q[n][k], X = sum_{k in g} x8[m][k], per output:
+ * P and X are exact int32 sums; the fold over groups, the scale by sx and
+ * the bias are float32, then y is rounded to bf16 (nearest, ties to even).
+ * Same weights (codes, scales, zeros) as w4a16_linear. Every M >= 1 runs
+ * on the tiled int8-MFMA kernel; K must be a multiple of 64.
+ *
+ * x8, sx  in   from quantize_act_int8 (may be NULL when M == 0)
+ * codes, scales, zeros, bias, N, K, G, y   as for w4a16_linear
+ */
+w4_status w4a8_linear(const int8_t *x8, const float *sx, int64_t M, const uint8_t *codes,
+                      const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
+                      int64_t N, int64_t K, int64_t G, uint16_t *y, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *w4_status_string(int status);
 

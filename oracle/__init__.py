@@ -1,6 +1,6 @@
 """CPU oracle for group-wise asymmetric int4 weight-only quantization, its
-fake-quantize round trip, the pre-shuffled weight layout, and the W4A16
-linear layer.
+fake-quantize round trip, the pre-shuffled weight layout, the W4A16
+linear layer, and the W4A8 path (per-token int8 activations).
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
 execute this package: only the test suite, the smoke check and the CPU
@@ -18,5 +18,7 @@ from .ref import (  # noqa: F401
     fake_quant_ref,
     linear_ref,
     linear_rows_ref,
+    act_quant_ref,
+    w4a8_linear_ref,
     rel_frobenius,
 )

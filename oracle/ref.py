@@ -32,6 +32,10 @@ Sources (web pages; cited by title and section):
     takes a packing format (a tile-packed one for one accelerator, a plain
     one for another); torchao release notes, "New Features": a pre-shuffled
     int4 tensor. No format is given (R17).
+  * torchao README: int8 dynamic activations with group-wise int4 weights
+    (the edge and QAT configuration; group size 32 in its example); "Optimum
+    Quanto", "Design overview / Tensors": int8 takes a symmetric projection
+    per tensor or per channel (R18).
 
 Readings taken where the pages leave the step open (each is listed in the
 design notes of the repository):
@@ -64,6 +68,11 @@ design notes of the repository):
       each 4-byte word (little endian) of a row holds the codes of 8
       consecutive k = 8j .. 8j+7 with nibble i = q[8j + 2i] and nibble
       4 + i = q[8j + 2i + 1] (i = 0..3), and sz[n, g] = s | z << 16.
+  R18 W4A8 activations: symmetric int8 per token (per row of x): a = max|x|,
+      sx = fl32(a / 127), x8 = clamp(rne(fl32(x / sx)), -127, 127), 0 when
+      a == 0 (binary32 division like R4, ties to even like R5). The linear
+      is y = sx * sum_g (s * sum x8 q + z * sum x8) (+ bias): the integer
+      sums are exact, the rest float64 here.
 """
 from __future__ import annotations
 
@@ -258,6 +267,51 @@ def linear_ref(x_bits, codes, scales_bits, zeros_bits, G: int,
     if bias_bits is not None:
         y += bf16_bits_to_f32(np.asarray(bias_bits, dtype=np.uint16)
                               ).astype(np.float64)[None, :]
+    return y
+
+
+def act_quant_ref(x_bits: np.ndarray):
+    """Per-token symmetric int8 of a bf16 x[M, K] (R18).
+
+    Returns (x8 int8 [M, K], sx float32 [M]). Division is numpy float32
+    (IEEE, correctly rounded); np.rint rounds half to even.
+    """
+    v = bf16_bits_to_f32(np.asarray(x_bits, dtype=np.uint16))
+    if v.ndim != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    a = np.abs(v).max(axis=1).astype(np.float32)
+    sx = (a / np.float32(127.0)).astype(np.float32)
+    zero = sx == np.float32(0.0)
+    ratio = np.divide(v, np.where(zero, np.float32(1.0), sx)[:, None],
+                      dtype=np.float32)
+    code = np.clip(np.rint(ratio), -127.0, 127.0)
+    code = np.where(zero[:, None], 0.0, code)
+    return code.astype(np.int8), sx
+
+
+def w4a8_linear_ref(x8, sx, codes, scales_bits, zeros_bits, G: int,
+                    bias_bits=None) -> np.ndarray:
+    """y = sx * sum_g (s * sum_{k in g} x8 q + z * sum_{k in g} x8) (+ bias),
+    float64, unrounded (R18). The per-group integer sums are formed in
+    float64, where they are exact (|sum| < 2**53)."""
+    x8 = np.asarray(x8, dtype=np.int8).astype(np.float64)
+    q = unpack_codes_ref(codes).astype(np.float64)
+    M, K = x8.shape
+    N = q.shape[0]
+    if q.shape[1] != K:
+        raise ValueError("x8 and codes disagree on K")
+    _check_group(K, G)
+    s = bf16_bits_to_f32(scales_bits).astype(np.float64)
+    z = bf16_bits_to_f32(zeros_bits).astype(np.float64)
+    acc = np.zeros((M, N), dtype=np.float64)
+    for g in range(K // G):
+        sl = slice(g * G, (g + 1) * G)
+        P = x8[:, sl] @ q[:, sl].T              # exact integers
+        X = x8[:, sl].sum(axis=1)               # exact integers
+        acc += P * s[None, :, g] + X[:, None] * z[None, :, g]
+    y = np.asarray(sx, dtype=np.float32).astype(np.float64)[:, None] * acc
+    if bias_bits is not None:
+        y = y + bf16_bits_to_f32(np.asarray(bias_bits, dtype=np.uint16)).astype(np.float64)
     return y
 
 

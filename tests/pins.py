@@ -288,6 +288,116 @@ def check_preshuffle(repack, W_codes_seed=17):
         assert np.array_equal(sz & 0xFFFF, s_bits) and np.array_equal(sz >> 16, z_bits)
 
 
+def _fl32_of(q: Fraction) -> Fraction:
+    """Exact binary32 rounding (nearest, ties to even) of a rational, normal
+    and subnormal range."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)                            # subnormals share the 2^-149 step
+    ulp = Fraction(2) ** (e - 23)
+    k = a / ulp
+    fl = k.numerator // k.denominator
+    rem = k - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * ulp
+
+
+def _rne_int(q: Fraction) -> int:
+    fl = q.numerator // q.denominator
+    rem = q - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return fl
+
+
+def check_act_quant(act_quant):
+    """Per-token int8 (R18) against exact rational arithmetic on small rows
+    (scale = binary32 rounding of max|x| / 127, codes = ties-to-even of the
+    binary32 rounding of x / scale, clamped), plus the invariants: |x8| <=
+    127, the row maximum maps to +-127, x8 * sx within sx / 2 of x, zero rows
+    give zeros, and negating x negates the codes."""
+    rng = np.random.default_rng(23)
+    V = rng.standard_normal((8, 64)) * 10.0 ** rng.integers(-4, 4, (8, 1))
+    V[2] = 0.0
+    V[3] = rng.uniform(-1.0, 1.0, 64)
+    V[3, :10] = [1.0, -0.5, 0.25, -0.75, 0.0, -0.0, 127.0, 63.5, 2.5, -3.5]   # scale 1: exact ties
+    V[4] = np.round(V[4] * 4) / 4
+    # half the row maximum lands within an ulp of 63.5: the binary32 quotient
+    # and a reciprocal multiply round to different codes here
+    V[5] = rng.uniform(-1.0, 1.0, 64)
+    V[5, :2] = [43.75, 21.875]
+    V[6] = rng.uniform(-1.0, 1.0, 64)
+    V[6, :2] = [-89.5, 44.75]
+    xb = bf16_from_float(V)
+    x8, sx = act_quant(xb)
+    assert x8.dtype == np.int8 and sx.dtype == np.float32 and x8.shape == V.shape
+    v = f32_from_bf16(xb)
+    for m in range(V.shape[0]):
+        a = max(abs(Fraction(float(t))) for t in v[m])
+        s_exact = _fl32_of(a / 127)
+        assert Fraction(float(sx[m])) == s_exact, f"row {m} scale"
+        for k in range(V.shape[1]):
+            if s_exact == 0:
+                want = 0
+            else:
+                want = max(-127, min(127, _rne_int(_fl32_of(Fraction(float(v[m, k])) / s_exact))))
+            assert int(x8[m, k]) == want, f"row {m} k {k}: {int(x8[m, k])} != {want}"
+    assert np.all(np.abs(x8.astype(np.int32)) <= 127)
+    live = sx > 0
+    amax_k = np.abs(v).argmax(axis=1)
+    assert np.all(np.abs(x8[np.arange(len(v)), amax_k][live].astype(np.int32)) == 127)
+    err = np.abs(x8.astype(np.float64) * sx[:, None].astype(np.float64) - v)
+    assert np.all(err <= sx[:, None].astype(np.float64) * (0.5 + 2.0**-20) + 1e-300)
+    assert np.all(x8[~live] == 0)
+    x8n, sxn = act_quant(bf16_from_float(-V))
+    assert np.array_equal(sxn, sx) and np.array_equal(x8n.astype(np.int32), -x8.astype(np.int32))
+
+
+def check_w4a8_linear(w4a8, linear, quantize):
+    """The W4A8 product (R18) two ways: exact rationals on a tiny case, and
+    a reduction to the pinned W4A16 oracle: with a power-of-two sx every
+    dequantized activation x8 * sx is a bf16 value, and the two products of
+    the same weights must agree."""
+    rng = np.random.default_rng(29)
+    M, N, K, G = 2, 3, 64, 32
+    W = bf16_from_float(rng.standard_normal((N, K)) * 0.05)
+    codes, s_bits, z_bits = quantize(W, G)
+    x8 = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    sx = np.array([0.0123, 2.5], dtype=np.float32)
+    bias = bf16_from_float(rng.standard_normal((1, N)))[0]
+    y = w4a8(x8, sx, codes, s_bits, z_bits, G, bias)
+    q = unpack_test(codes)
+    sF = [[Fraction(float(t)) for t in r] for r in f32_from_bf16(s_bits)]
+    zF = [[Fraction(float(t)) for t in r] for r in f32_from_bf16(z_bits)]
+    bF = [Fraction(float(t)) for t in f32_from_bf16(bias)]
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for g in range(K // G):
+                P = sum(int(x8[m, k]) * int(q[n, k]) for k in range(g * G, (g + 1) * G))
+                X = sum(int(x8[m, k]) for k in range(g * G, (g + 1) * G))
+                tot += sF[n][g] * P + zF[n][g] * X
+            exact = Fraction(float(sx[m])) * tot + bF[n]
+            assert abs(Fraction(float(y[m, n])) - exact) <= abs(exact) * Fraction(1, 10**12), (m, n)
+    M, N, K, G = 5, 40, 256, 64
+    W = bf16_from_float(rng.standard_normal((N, K)) * 0.05)
+    codes, s_bits, z_bits = quantize(W, G)
+    x8 = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    sx = np.float32(2.0) ** rng.integers(-12, -4, M).astype(np.float32)
+    xh = bf16_from_float(x8.astype(np.float64) * sx[:, None].astype(np.float64))
+    assert np.array_equal(f32_from_bf16(xh).astype(np.float64),
+                          x8.astype(np.float64) * sx[:, None].astype(np.float64))
+    y1 = w4a8(x8, sx.astype(np.float32), codes, s_bits, z_bits, G)
+    y2 = linear(xh, codes, s_bits, z_bits, G)
+    assert np.allclose(y1, y2, rtol=1e-12, atol=1e-12 * np.abs(y2).max())
+
+
 def run_all_pins(mod):
     """Every pin against an oracle module-like object."""
     check_bf16_helper(mod.f32_to_bf16_bits)
@@ -308,3 +418,6 @@ def run_all_pins(mod):
         check_fake_quant(mod.fake_quant_ref, mod.quantize_ref, bf16_from_float(V), 32)
     if hasattr(mod, "repack_preshuffled_ref"):
         check_preshuffle(mod.repack_preshuffled_ref)
+    if hasattr(mod, "act_quant_ref"):
+        check_act_quant(mod.act_quant_ref)
+        check_w4a8_linear(mod.w4a8_linear_ref, mod.linear_ref, mod.quantize_ref)

@@ -32,7 +32,8 @@ def test_header_declares_expected_entry_points():
     assert declared_functions() == sorted([
         "quantize_int4_grouped", "fake_quant_int4_grouped", "w4a16_linear",
         "w4a16_linear_select", "repack_int4_preshuffled", "w4a16_linear_preshuffled",
-        "w4a16_linear_preshuffled_select", "w4_status_string"])
+        "w4a16_linear_preshuffled_select", "quantize_act_int8", "w4a8_linear",
+        "w4_status_string"])
 
 
 def test_library_exports_every_declared_function(L):
@@ -190,6 +191,44 @@ def test_linear_preshuffled_auto_entry_point_validates(L):
     assert L.w4a16_linear_preshuffled(A, 1, B, None, None, 64, 128, 32, E, None) == \
         w4.W4Status.ERR_NULL
     assert L.w4a16_linear_preshuffled(A, 0, B, C, None, 64, 128, 32, E, None) == w4.W4Status.OK
+
+
+def aq(L, x=A, M=4, K=64, x8=B, sx=C):
+    return L.quantize_act_int8(x, M, K, x8, sx, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(x=None), w4.W4Status.ERR_NULL),
+    (dict(sx=None), w4.W4Status.ERR_NULL),
+    (dict(K=48), w4.W4Status.ERR_SHAPE),
+    (dict(K=16), w4.W4Status.ERR_SHAPE),
+    (dict(M=-1), w4.W4Status.ERR_SHAPE),
+    (dict(x8=B + 8), w4.W4Status.ERR_ALIGN),
+    (dict(sx=C + 4), w4.W4Status.ERR_ALIGN),
+    (dict(x8=A + 64), w4.W4Status.ERR_ALIAS),                # x8 inside x
+    (dict(sx=B), w4.W4Status.ERR_ALIAS),                     # sx over x8
+    (dict(M=0, x=None, x8=None, sx=None), w4.W4Status.OK),
+])
+def test_act_quant_validation(L, kw, expect):
+    assert aq(L, **kw) == expect
+
+
+def w8(L, x8=A, sx=B, M=4, codes=C, s=D, z=E, bias=None, N=64, K=128, G=32, y=E + (1 << 31)):
+    return L.w4a8_linear(x8, sx, M, codes, s, z, bias, N, K, G, y, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(codes=None), w4.W4Status.ERR_NULL),
+    (dict(sx=None), w4.W4Status.ERR_NULL),
+    (dict(K=96), w4.W4Status.ERR_SHAPE),                     # K % 64 != 0
+    (dict(G=100), w4.W4Status.ERR_GROUP),
+    (dict(M=-1), w4.W4Status.ERR_SHAPE),
+    (dict(sx=B + 4), w4.W4Status.ERR_ALIGN),
+    (dict(y=C), w4.W4Status.ERR_ALIAS),                      # y over codes
+    (dict(M=0, x8=None, sx=None, y=None), w4.W4Status.OK),
+])
+def test_w4a8_validation(L, kw, expect):
+    assert w8(L, **kw) == expect
 
 
 def test_binding_rejects_host_tensors():

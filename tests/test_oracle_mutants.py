@@ -51,6 +51,22 @@ MUTANTS = {
     "preshuffle_natural_nibbles": (
         "nib = np.concatenate([words[:, :, 0::2], words[:, :, 1::2]], axis=2)",
         "nib = words"),
+    "act_scale_over_128": (
+        "sx = (a / np.float32(127.0)).astype(np.float32)",
+        "sx = (a / np.float32(128.0)).astype(np.float32)"),
+    "act_round_half_up": ("code = np.clip(np.rint(ratio), -127.0, 127.0)",
+                          "code = np.clip(np.floor(ratio + 0.5), -127.0, 127.0)"),
+    "act_truncate": ("code = np.clip(np.rint(ratio), -127.0, 127.0)",
+                     "code = np.clip(np.trunc(ratio), -127.0, 127.0)"),
+    "act_reciprocal_multiply": (
+        "ratio = np.divide(v, np.where(zero, np.float32(1.0), sx)[:, None],\n                      dtype=np.float32)",
+        "ratio = np.multiply(v, (np.float32(1.0) / np.where(zero, np.float32(1.0), sx))[:, None],\n                        dtype=np.float32)"),
+    "w4a8_drops_zero_term": ("acc += P * s[None, :, g] + X[:, None] * z[None, :, g]",
+                             "acc += P * s[None, :, g]"),
+    "w4a8_no_token_scale": (
+        "y = np.asarray(sx, dtype=np.float32).astype(np.float64)[:, None] * acc",
+        "y = acc.copy()"),
+    "w4a8_group_shift": ("sl = slice(g * G, (g + 1) * G)", "sl = slice(g * G + 1, (g + 1) * G + 1)"),
     "preshuffle_sz_swapped": (
         "return codes_ps, (s | (z << np.uint32(16))).astype(np.uint32)",
         "return codes_ps, (z | (s << np.uint32(16))).astype(np.uint32)"),
