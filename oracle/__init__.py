@@ -1,6 +1,7 @@
 """CPU oracle for group-wise asymmetric int4 weight-only quantization, its
 fake-quantize round trip, the pre-shuffled weight layout, the W4A16
-linear layer, and the W4A8 path (per-token int8 activations).
+linear layer, the W4A8 path (per-token int8 activations), and int8
+weight-only quantization with its linear.
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or
 execute this package: only the test suite, the smoke check and the CPU
@@ -19,6 +20,8 @@ from .ref import (  # noqa: F401
     linear_ref,
     linear_rows_ref,
     act_quant_ref,
+    quantize_int8_ref,
+    linear_int8_ref,
     w4a8_linear_ref,
     rel_frobenius,
 )

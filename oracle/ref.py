@@ -36,6 +36,9 @@ Sources (web pages; cited by title and section):
     (the edge and QAT configuration; group size 32 in its example); "Optimum
     Quanto", "Design overview / Tensors": int8 takes a symmetric projection
     per tensor or per channel (R18).
+  * torchao README and its diffusers example: an int8 weight-only config
+    with per-group granularity, group size 128; the release notes page
+    (0.9.0 API change): the same config as ``group_size=128`` (R19).
 
 Readings taken where the pages leave the step open (each is listed in the
 design notes of the repository):
@@ -73,6 +76,11 @@ design notes of the repository):
       a == 0 (binary32 division like R4, ties to even like R5). The linear
       is y = sx * sum_g (s * sum x8 q + z * sum x8) (+ bias): the integer
       sums are exact, the rest float64 here.
+  R19 int8 weight-only: symmetric (the Quanto projection for int8) per group
+      of G along K: a = max |v| over the group, s = bf16_rne(fl32(a / 127)),
+      q = clamp(rne(fl32(v / s)), -127, 127) with the stored scale (as R3,
+      R4, R5), 0 when s == 0; w_hat = q * s; codes int8 [N, K], scales bf16
+      [N, K/G].
 """
 from __future__ import annotations
 
@@ -267,6 +275,43 @@ def linear_ref(x_bits, codes, scales_bits, zeros_bits, G: int,
     if bias_bits is not None:
         y += bf16_bits_to_f32(np.asarray(bias_bits, dtype=np.uint16)
                               ).astype(np.float64)[None, :]
+    return y
+
+
+def quantize_int8_ref(W_bits: np.ndarray, G: int):
+    """Group-wise symmetric int8 weight-only quantization of a bf16 W[N, K]
+    (R19). Returns (codes int8 [N, K], scales uint16 bf16 bits [N, K/G])."""
+    W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    if W_bits.ndim != 2:
+        raise ValueError("W must be 2-D [N, K]")
+    N, K = W_bits.shape
+    _check_group(K, G)
+    v = bf16_bits_to_f32(W_bits).reshape(N, K // G, G)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("R10: non-finite weight")
+    amax = np.abs(v).max(axis=2).astype(np.float32)
+    scale_bits = f32_to_bf16_bits((amax / np.float32(127.0)).astype(np.float32))
+    sc = np.broadcast_to(bf16_bits_to_f32(scale_bits)[:, :, None], v.shape)
+    dead = sc == np.float32(0.0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.divide(v, np.where(dead, np.float32(1.0), sc), dtype=np.float32)
+    q8 = np.where(dead, 0.0, np.clip(np.rint(t), -127.0, 127.0))
+    return q8.astype(np.int8).reshape(N, K), scale_bits
+
+
+def linear_int8_ref(x_bits, codes8, scales_bits, G: int, bias_bits=None) -> np.ndarray:
+    """y = x . w_hat^T (+ bias), w_hat = q * s (exact), float64, unrounded."""
+    x = bf16_bits_to_f32(np.asarray(x_bits, dtype=np.uint16)).astype(np.float64)
+    q8 = np.asarray(codes8, dtype=np.int8).astype(np.float64)
+    N, K = q8.shape
+    _check_group(K, G)
+    if x.shape[1] != K:
+        raise ValueError("x and codes disagree on K")
+    sc = bf16_bits_to_f32(scales_bits).astype(np.float64)
+    w = q8 * np.repeat(sc, G, axis=1)
+    y = x @ w.T
+    if bias_bits is not None:
+        y = y + bf16_bits_to_f32(np.asarray(bias_bits, dtype=np.uint16)).astype(np.float64)
     return y
 
 

@@ -398,6 +398,76 @@ def check_w4a8_linear(w4a8, linear, quantize):
     assert np.allclose(y1, y2, rtol=1e-12, atol=1e-12 * np.abs(y2).max())
 
 
+def _bf16_of_f32(x: Fraction) -> Fraction:
+    """Exact bf16 rounding (nearest, ties to even) of a binary32 value."""
+    if x == 0:
+        return Fraction(0)
+    sign = -1 if x < 0 else 1
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, -126)
+    ulp = Fraction(2) ** (e - 7)
+    k = a / ulp
+    fl = k.numerator // k.denominator
+    rem = k - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * fl * ulp
+
+
+def check_int8_weights(quantize8, linear8):
+    """Int8 weight-only (R19): scales and codes against exact rationals
+    (binary32 rounding of max|v| / 127, then bf16 rounding; binary32 rounding
+    of v / s, ties to even, clamp), invariants (|q| <= 127, |q s - v| <= s/2,
+    zero groups give 0, negating W negates the codes), and the linear
+    against an independent float64 product with W itself on weights that are
+    exact multiples q * s of a power-of-two scale."""
+    rng = np.random.default_rng(31)
+    for G in (32, 128):
+        V = rng.standard_normal((4, 2 * G)) * 10.0 ** rng.integers(-3, 3, (4, 1))
+        V[1, :G] = 0.0
+        V[2, :8] = [127.0, 63.5, -0.5, 2.5, -3.5, 0.0, -0.0, 1.5]
+        V[2, 8:G] = rng.uniform(-1.0, 1.0, G - 8)
+        Wb = bf16_from_float(V)
+        q, sb = quantize8(Wb, G)
+        assert q.dtype == np.int8 and q.shape == V.shape and sb.dtype == np.uint16
+        v = f32_from_bf16(Wb)
+        sf = f32_from_bf16(sb)
+        for n in range(V.shape[0]):
+            for g in range(V.shape[1] // G):
+                grp = [Fraction(float(t)) for t in v[n, g * G:(g + 1) * G]]
+                s_exact = _bf16_of_f32(_fl32_of(max(abs(t) for t in grp) / 127))
+                assert Fraction(float(sf[n, g])) == s_exact, (G, n, g)
+                for j, t in enumerate(grp):
+                    want = 0 if s_exact == 0 else max(-127, min(127, _rne_int(_fl32_of(t / s_exact))))
+                    assert int(q[n, g * G + j]) == want, (G, n, g, j)
+        w = np.repeat(sf.astype(np.float64), G, axis=1)
+        assert np.all(np.abs(q.astype(np.int32)) <= 127)
+        assert np.all(np.abs(q * w - v) <= w * (0.5 + 2.0**-20) + 1e-300)
+        assert np.all(q[1, :G] == 0) and np.all(sb[1, 0] == 0)
+        qn, sbn = quantize8(bf16_from_float(-V), G)
+        assert np.array_equal(sbn, sb) and np.array_equal(qn.astype(np.int32), -q.astype(np.int32))
+    # linear on exact grid weights: W = q * 2^-e per group
+    M, N, K, G = 3, 20, 256, 64
+    qg = rng.integers(-127, 128, (N, K))
+    qg[np.arange(N), rng.integers(0, K, N)] = 127          # every row reaches the max
+    qg[:, ::G] = 127                                       # every group too
+    e = rng.integers(6, 12, (N, K // G))
+    W = qg * (2.0 ** -np.repeat(e, G, axis=1))
+    Wb = bf16_from_float(W)
+    assert np.array_equal(f32_from_bf16(Wb).astype(np.float64), W)
+    q, sb = quantize8(Wb, G)
+    assert np.array_equal(q.astype(np.int64), qg), "grid weights must encode exactly"
+    x = bf16_from_float(rng.standard_normal((M, K)))
+    bias = bf16_from_float(rng.standard_normal((1, N)))[0]
+    y = linear8(x, q, sb, G, bias)
+    theirs = (torch.from_numpy(f32_from_bf16(x).astype(np.float64)) @
+              torch.from_numpy(W).T).numpy() + f32_from_bf16(bias).astype(np.float64)
+    assert np.allclose(y, theirs, rtol=1e-12, atol=1e-12 * np.abs(theirs).max())
+
+
 def run_all_pins(mod):
     """Every pin against an oracle module-like object."""
     check_bf16_helper(mod.f32_to_bf16_bits)
@@ -418,6 +488,8 @@ def run_all_pins(mod):
         check_fake_quant(mod.fake_quant_ref, mod.quantize_ref, bf16_from_float(V), 32)
     if hasattr(mod, "repack_preshuffled_ref"):
         check_preshuffle(mod.repack_preshuffled_ref)
+    if hasattr(mod, "quantize_int8_ref"):
+        check_int8_weights(mod.quantize_int8_ref, mod.linear_int8_ref)
     if hasattr(mod, "act_quant_ref"):
         check_act_quant(mod.act_quant_ref)
         check_w4a8_linear(mod.w4a8_linear_ref, mod.linear_ref, mod.quantize_ref)

@@ -67,6 +67,16 @@ MUTANTS = {
         "y = np.asarray(sx, dtype=np.float32).astype(np.float64)[:, None] * acc",
         "y = acc.copy()"),
     "w4a8_group_shift": ("sl = slice(g * G, (g + 1) * G)", "sl = slice(g * G + 1, (g + 1) * G + 1)"),
+    "int8_scale_over_128": ("f32_to_bf16_bits((amax / np.float32(127.0)).astype(np.float32))",
+                            "f32_to_bf16_bits((amax / np.float32(128.0)).astype(np.float32))"),
+    "int8_scale_unrounded": (
+        "sc = np.broadcast_to(bf16_bits_to_f32(scale_bits)[:, :, None], v.shape)",
+        "sc = np.broadcast_to((amax / np.float32(127.0)).astype(np.float32)[:, :, None], v.shape)"),
+    "int8_round_half_up": ("np.clip(np.rint(t), -127.0, 127.0)", "np.clip(np.floor(t + 0.5), -127.0, 127.0)"),
+    "int8_linear_scale_tiled": ("w = q8 * np.repeat(sc, G, axis=1)", "w = q8 * np.tile(sc, (1, G))"),
+    "int8_linear_no_bias": (
+        "        y = y + bf16_bits_to_f32(np.asarray(bias_bits, dtype=np.uint16)).astype(np.float64)\n    return y\n\n\ndef act_quant_ref",
+        "        y = y + 0.0\n    return y\n\n\ndef act_quant_ref"),
     "preshuffle_sz_swapped": (
         "return codes_ps, (s | (z << np.uint32(16))).astype(np.uint32)",
         "return codes_ps, (z | (s << np.uint32(16))).astype(np.uint32)"),
