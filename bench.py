@@ -183,7 +183,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "step", "gemv", "gemv16", "gemm", "quantize", "fake", "ps", "w4a8",
-                                       "copy"],
+                                       "w8a16", "copy"],
                     default="all", help="restrict to one part (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -496,6 +496,83 @@ def main():
                               "achieved_GBps": round(tot_aq_b / (tot_aq_ms * 1e-3) / 1e9, 1),
                               "set_us": round(tot_aq_ms * 1e3, 2)},
             }
+
+    # ---- int8 weight-only: quantizer, decode (M = 1) and prefill (M = 2048) --
+    if args.only in ("all", "w8a16"):
+        def w8_bytes(M, N, K, Gq):
+            return N * K + 2 * N * (K // Gq) + 2 * M * K + 2 * M * N
+
+        gb8 = sum(w8_bytes(1, N, K, G) for N, K in layers.values())
+        n8 = max(2, -(-ROTATE_BYTES // gb8))
+        log(f"w8a16 decode: {n8} rotating copies of {gb8 / 1e6:.1f} MB")
+        per = {}
+        tot_ms = tot_q_ms = 0.0
+        tot_b = tot_q_b = 0
+        for li, (name, (N, K)) in enumerate(layers.items()):
+            copies = []
+            for r in range(n8):
+                src = sets[r % n_sets][name]
+                q8, s8 = w4.quantize_int8_grouped(src[0], G)
+                copies.append((src[0], src[1], q8, s8,
+                               torch.empty((1, N), dtype=torch.bfloat16, device=dev)))
+            g = graph_of(torch, [(lambda e=e: w4.w8a16_linear(e[1], e[2], e[3], G, out=e[4]))
+                                 for e in copies])
+            ms = time_graphs(torch, [g], max(2, reps // 2)) / n8
+            del g
+            g = graph_of(torch, [(lambda e=e: w4.quantize_int8_grouped(e[0], G, e[2], e[3]))
+                                 for e in copies])
+            ms_q = time_graphs(torch, [g], max(2, reps // 2)) / n8
+            del g
+            b = w8_bytes(1, N, K, G)
+            bq = 3 * N * K + 2 * N * (K // G)
+            per[name] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                         "quantize_us": round(ms_q * 1e3, 3),
+                         "quantize_GBps": round(bq / (ms_q * 1e-3) / 1e9, 1)}
+            tot_ms += ms
+            tot_b += b
+            tot_q_ms += ms_q
+            tot_q_b += bq
+            del copies
+        out["w8a16_gemv_m1"] = {
+            "kernel": "w8a16_gemv_kernel<128>", "bound": "hbm",
+            "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
+            "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
+            "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_set": tot_b, "per_layer": per,
+        }
+        out["quantize8_g128"] = {
+            "kernel": "quantize8_kernel<128>", "bound": "hbm",
+            "achieved_GBps": round(tot_q_b / (tot_q_ms * 1e-3) / 1e9, 1),
+            "frac": round(tot_q_b / (tot_q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_set": tot_q_b,
+        }
+        M = 2048
+        glayers = dict(workloads.GEMMA3_12B)
+        log("w8a16 prefill: Gemma3-12B-shaped layers, M=2048")
+        per = {}
+        tot_ms = 0.0
+        tot_f = 0
+        for i, (name, (N, K)) in enumerate(glayers.items()):
+            W, x = make_layer(torch, N, K, 50 + i, M, dev)
+            q8, s8 = w4.quantize_int8_grouped(W, G)
+            del W
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            fn = (lambda x=x, q8=q8, s8=s8, y=y: w4.w8a16_linear(x, q8, s8, G, out=y))
+            fn()
+            g = graph_of(torch, [fn])
+            ms = time_graphs(torch, [g], max(3, reps // 5))
+            del g
+            f = 2 * M * N * K
+            per[name] = {"us": round(ms * 1e3, 2), "TFLOPs": round(f / (ms * 1e-3) / 1e12, 1)}
+            tot_ms += ms
+            tot_f += f
+            del x, q8, s8, y
+        out["w8a16_gemm_m2048"] = {
+            "kernel": "w8a16_gemm_kernel<128>", "bound": "mfma",
+            "achieved_TFLOPs": round(tot_f / (tot_ms * 1e-3) / 1e12, 1),
+            "frac": round(tot_f / (tot_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops_per_set": tot_f, "set_us": round(tot_ms * 1e3, 2), "per_layer": per,
+        }
 
     # ---- achievable-bandwidth reference: torch's own device copy ----------
     # The same buffers calibrate the HBM byte counters: an elementwise

@@ -17,6 +17,7 @@ from .build import LIB_PATH
 __all__ = [
     "W4Status", "W4Path", "W4Error", "GROUP_SIZES", "GEMV_MAX_M", "lib",
     "repack_int4_preshuffled", "w4a16_linear_preshuffled", "quantize_act_int8", "w4a8_linear",
+    "quantize_int8_grouped", "w8a16_linear",
     "quantize_int4_grouped", "fake_quant_int4_grouped", "w4a16_linear", "status_string",
 ]
 
@@ -80,6 +81,10 @@ def lib() -> ctypes.CDLL:
         L.quantize_act_int8.restype = _int
         L.w4a8_linear.argtypes = [_p, _p, _i64, _p, _p, _p, _p, _i64, _i64, _i64, _p, _p]
         L.w4a8_linear.restype = _int
+        L.quantize_int8_grouped.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p]
+        L.quantize_int8_grouped.restype = _int
+        L.w8a16_linear.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _p]
+        L.w8a16_linear.restype = _int
         L.w4_status_string.argtypes = [_int]
         L.w4_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -294,4 +299,50 @@ def w4a8_linear(x8, sx, codes, scales, zeros, G: int, bias=None, out=None):
                            out.data_ptr(), _stream_ptr(x8.device))
     if st != W4Status.OK:
         raise W4Error(st, "w4a8_linear")
+    return out
+
+
+def quantize_int8_grouped(W, G: int, codes8=None, scales=None):
+    """Group-wise symmetric int8 of a bf16 GPU W[N, K]; returns (codes8 int8
+    [N, K], scales bf16 [N, K/G])."""
+    torch = _torch()
+    if W.dim() != 2:
+        raise ValueError("W must be 2-D [N, K]")
+    N, K = W.shape
+    ng = K // G if G else 0
+    _check(W, "W", torch.bfloat16, (N, K))
+    if codes8 is None:
+        codes8 = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    if scales is None:
+        scales = torch.empty((N, ng), dtype=torch.bfloat16, device=W.device)
+    _check(codes8, "codes8", torch.int8, (N, K), W.device)
+    _check(scales, "scales", torch.bfloat16, (N, ng), W.device)
+    st = lib().quantize_int8_grouped(W.data_ptr(), N, K, G, codes8.data_ptr(), scales.data_ptr(),
+                                     _stream_ptr(W.device))
+    if st != W4Status.OK:
+        raise W4Error(st, "quantize_int8_grouped")
+    return codes8, scales
+
+
+def w8a16_linear(x, codes8, scales, G: int, bias=None, out=None):
+    """y = x . (q s)^T (+ bias) for bf16 GPU x[M, K] and int8 weights."""
+    torch = _torch()
+    if x.dim() != 2 or codes8.dim() != 2:
+        raise ValueError("x and codes8 must be 2-D")
+    M, K = x.shape
+    N = codes8.shape[0]
+    ng = K // G if G else 0
+    _check(x, "x", torch.bfloat16, (M, K))
+    _check(codes8, "codes8", torch.int8, (N, K), x.device)
+    _check(scales, "scales", torch.bfloat16, (N, ng), x.device)
+    if bias is not None:
+        _check(bias, "bias", torch.bfloat16, (N,), x.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(out, "out", torch.bfloat16, (M, N), x.device)
+    st = lib().w8a16_linear(x.data_ptr(), M, codes8.data_ptr(), scales.data_ptr(),
+                            bias.data_ptr() if bias is not None else None, N, K, G,
+                            out.data_ptr(), _stream_ptr(x.device))
+    if st != W4Status.OK:
+        raise W4Error(st, "w8a16_linear")
     return out

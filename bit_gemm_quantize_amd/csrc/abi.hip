@@ -190,6 +190,43 @@ w4_status w4a8_linear(const int8_t *x8, const float *sx, int64_t M, const uint8_
     return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
 
+w4_status quantize_int8_grouped(const uint16_t *W, int64_t N, int64_t K, int64_t G,
+                                int8_t *codes8, uint16_t *scales, hipStream_t stream) {
+    if (!W || !codes8 || !scales) return W4_ERR_NULL;
+    const w4_status st = check_nkg(N, K, G);
+    if (st != W4_OK) return st;
+    if (!aligned16(W) || !aligned16(codes8) || !aligned16(scales)) return W4_ERR_ALIGN;
+    const int64_t wbytes = 2 * N * K, gbytes = 2 * N * (K / G);
+    if (overlap(codes8, N * K, W, wbytes) || overlap(scales, gbytes, W, wbytes) ||
+        overlap(codes8, N * K, scales, gbytes))
+        return W4_ERR_ALIAS;
+    const hipError_t e = w4::launch_quantize8(W, N, K, static_cast<int>(G), codes8, scales,
+                                              stream);
+    return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
+w4_status w8a16_linear(const uint16_t *x, int64_t M, const int8_t *codes8,
+                       const uint16_t *scales, const uint16_t *bias, int64_t N, int64_t K,
+                       int64_t G, uint16_t *y, hipStream_t stream) {
+    if (!codes8 || !scales) return W4_ERR_NULL;
+    if (M > 0 && (!x || !y)) return W4_ERR_NULL;
+    if (M < 0 || M > kMaxM) return W4_ERR_SHAPE;
+    const w4_status st = check_nkg(N, K, G);
+    if (st != W4_OK) return st;
+    if (K % 64 != 0 || M * K > kMaxElems || M * N > kMaxElems) return W4_ERR_SHAPE;
+    if (!aligned16(codes8) || !aligned16(scales) || (bias && !aligned16(bias)))
+        return W4_ERR_ALIGN;
+    if (M > 0 && (!aligned16(x) || !aligned16(y))) return W4_ERR_ALIGN;
+    if (M == 0) return W4_OK;
+    const int64_t ybytes = 2 * M * N;
+    if (overlap(y, ybytes, x, 2 * M * K) || overlap(y, ybytes, codes8, N * K) ||
+        overlap(y, ybytes, scales, 2 * N * (K / G)) || overlap(y, ybytes, bias, 2 * N))
+        return W4_ERR_ALIAS;
+    const hipError_t e = w4::launch_w8a16(x, M, codes8, scales, bias, N, K, static_cast<int>(G),
+                                          y, stream);
+    return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
 const char *w4_status_string(int status) {
     switch (status) {
     case W4_OK: return "W4_OK: success";

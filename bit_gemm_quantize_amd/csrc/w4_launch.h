@@ -35,6 +35,14 @@ hipError_t launch_w4a8_gemm(const int8_t *x8, const float *sx, int64_t M, const 
                             const uint16_t *bias, int64_t N, int64_t K, int G, uint16_t *y,
                             hipStream_t stream);
 
+// Int8 weight-only: quantizer (codes int8 [N, K], scales [N, K/G]) and the
+// linear for any M >= 1 (K % 64 == 0).
+hipError_t launch_quantize8(const uint16_t *W, int64_t N, int64_t K, int G, int8_t *q8,
+                            uint16_t *scales, hipStream_t stream);
+hipError_t launch_w8a16(const uint16_t *x, int64_t M, const int8_t *q8, const uint16_t *scales,
+                        const uint16_t *bias, int64_t N, int64_t K, int G, uint16_t *y,
+                        hipStream_t stream);
+
 // Decode GEMV, 1 <= M <= 16. Plain layout (scales, zeros; sz == NULL) or
 // pre-shuffled layout (codes pre-shuffled, sz != NULL; scales, zeros unused).
 hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *codes,

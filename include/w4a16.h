@@ -237,6 +237,35 @@ w4_status w4a8_linear(const int8_t *x8, const float *sx, int64_t M, const uint8_
                       const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
                       int64_t N, int64_t K, int64_t G, uint16_t *y, hipStream_t stream);
 
+/*
+ * Int8 weight-only (torchao README and its diffusers example: an int8
+ * weight-only config with per-group granularity, group size 128; the
+ * release notes' 0.9.0 API change names the same config with group_size=128;
+ * "Optimum Quanto", "Design overview / Tensors": int8 takes a symmetric
+ * projection).
+ *
+ * quantize_int8_grouped - per group g of G consecutive k of row n:
+ *   a = max |v|;  s = bf16_rne(fl32(a / 127));
+ *   q = clamp(rne(fl32(v / s)), -127, 127), 0 when s == 0
+ * (IEEE binary32 division by the stored scale, ties to even). Bit-exact.
+ *
+ * W       in   bf16 [N, K]; N, K, G as for quantize_int4_grouped
+ * codes8  out  int8 [N, K]; scales out bf16 [N, K/G]; no overlaps
+ */
+w4_status quantize_int8_grouped(const uint16_t *W, int64_t N, int64_t K, int64_t G,
+                                int8_t *codes8, uint16_t *scales, hipStream_t stream);
+
+/*
+ * w8a16_linear - y = x . w_hat^T (+ bias), w_hat = q * s (exact), each output
+ * accumulated in float32 as sum_g s[n][g] * sum_{k in g} x[m][k] q[n][k] and
+ * rounded to bf16. M <= 16 (and K <= 2^24) runs a split-K kernel, else a tiled MFMA
+ * kernel; K must be a multiple of 64. Arguments as w4a16_linear with codes8
+ * and scales from quantize_int8_grouped.
+ */
+w4_status w8a16_linear(const uint16_t *x, int64_t M, const int8_t *codes8,
+                       const uint16_t *scales, const uint16_t *bias, int64_t N, int64_t K,
+                       int64_t G, uint16_t *y, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *w4_status_string(int status);
 

@@ -33,7 +33,7 @@ def test_header_declares_expected_entry_points():
         "quantize_int4_grouped", "fake_quant_int4_grouped", "w4a16_linear",
         "w4a16_linear_select", "repack_int4_preshuffled", "w4a16_linear_preshuffled",
         "w4a16_linear_preshuffled_select", "quantize_act_int8", "w4a8_linear",
-        "w4_status_string"])
+        "quantize_int8_grouped", "w8a16_linear", "w4_status_string"])
 
 
 def test_library_exports_every_declared_function(L):
@@ -229,6 +229,46 @@ def w8(L, x8=A, sx=B, M=4, codes=C, s=D, z=E, bias=None, N=64, K=128, G=32, y=E 
 ])
 def test_w4a8_validation(L, kw, expect):
     assert w8(L, **kw) == expect
+
+
+def q8(L, W=A, N=16, K=128, G=32, codes=B, s=C):
+    return L.quantize_int8_grouped(W, N, K, G, codes, s, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(W=None), w4.W4Status.ERR_NULL),
+    (dict(codes=None), w4.W4Status.ERR_NULL),
+    (dict(s=None), w4.W4Status.ERR_NULL),
+    (dict(G=48), w4.W4Status.ERR_GROUP),
+    (dict(K=96, G=64), w4.W4Status.ERR_SHAPE),               # K % G != 0
+    (dict(N=0), w4.W4Status.ERR_SHAPE),
+    (dict(codes=B + 8), w4.W4Status.ERR_ALIGN),
+    (dict(codes=A + 1024), w4.W4Status.ERR_ALIAS),           # codes inside W
+    (dict(s=B + 1024), w4.W4Status.ERR_ALIAS),               # scales inside codes
+])
+def test_quantize_int8_validation(L, kw, expect):
+    assert q8(L, **kw) == expect
+
+
+def l8(L, x=A, M=4, codes=B, s=C, bias=None, N=64, K=128, G=32, y=E):
+    return L.w8a16_linear(x, M, codes, s, bias, N, K, G, y, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(codes=None), w4.W4Status.ERR_NULL),
+    (dict(s=None), w4.W4Status.ERR_NULL),
+    (dict(x=None), w4.W4Status.ERR_NULL),
+    (dict(K=96), w4.W4Status.ERR_SHAPE),                     # K % 64 != 0
+    (dict(G=100), w4.W4Status.ERR_GROUP),
+    (dict(M=-1), w4.W4Status.ERR_SHAPE),
+    (dict(bias=D + 2), w4.W4Status.ERR_ALIGN),
+    (dict(y=E + 8), w4.W4Status.ERR_ALIGN),
+    (dict(y=B), w4.W4Status.ERR_ALIAS),                      # y over codes
+    (dict(y=A + 64), w4.W4Status.ERR_ALIAS),                 # y inside x
+    (dict(M=0, x=None, y=None), w4.W4Status.OK),
+])
+def test_w8a16_validation(L, kw, expect):
+    assert l8(L, **kw) == expect
 
 
 def test_binding_rejects_host_tensors():
