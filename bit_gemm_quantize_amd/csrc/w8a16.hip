@@ -24,6 +24,7 @@
 // read x and the codes straight from memory (loads for the next four
 // 32-wide slices in flight) and reduce their partial sums in LDS.
 #include <type_traits>
+#include <utility>
 
 #include "w4_device.h"
 #include "w4_launch.h"
@@ -102,6 +103,12 @@ constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SZ_BYTES;
 
 template <int V>
 using IC = std::integral_constant<int, V>;
+
+// f(IC<0>{}), f(IC<1>{}), ...: a loop unrolled with compile-time indices
+template <typename F, int... I>
+__device__ __forceinline__ void unrolled(std::integer_sequence<int, I...>, F &&f) {
+    (f(IC<I>{}), ...);
+}
 
 __device__ __forceinline__ void copy16(const void *g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
@@ -288,25 +295,37 @@ __global__ __launch_bounds__(THREADS, 2) void w8a16_gemm_kernel(
 
 // ---------------------------------------------------------------- GEMV, M <= 16
 constexpr int GV8_WAVES = 8;
-constexpr int GV8_DEPTH = 4;                     // 32-wide slices in flight per wave
+constexpr int GV8_DEPTH = 4;                     // 64-wide slices in flight per wave
 
-// Block: 16 output columns n0 .. n0 + 15; wave w takes slices w, w + 8, ...
-// of K (32 wide). Lane (nl, kb): A row nl (x row, rows >= M repeat M - 1 and
-// are never stored), B column n0 + nl, k = 32 j + 8 kb .. + 8.
+// Block: 16 output columns n0 .. n0 + 15; the 8 waves split K in slices of
+// 64 k. Lane (nl, kb): A row nl (x row; rows >= M repeat M - 1 and are never
+// stored), B column n0 + nl, code bytes 16 kb .. + 16 of the slice: one
+// 16-byte load per lane covers 64 contiguous bytes of each of 16 rows. The
+// MFMA (16 x 16 x 32) takes 8 k per lane; any assignment of the slice's k to
+// lanes works if the x operand follows it and one MFMA never mixes groups:
+//   G >= 64: a wave takes whole groups (groups w, w + 8, ...); the slice feeds
+//     two MFMAs, on bytes 0..7 and 8..15 of each lane;
+//   G = 32: a slice is two groups (kb 0, 1 hold the first, kb 2, 3 the
+//     second); swapping the upper 8 bytes of lanes kb 0, 1 with the lower 8
+//     of lanes kb 2, 3 (permlane32 swaps) gives every lane 8 bytes of each
+//     group: the first MFMA sees k = 16 (kb % 2) + 8 (kb / 2) .. + 8, the
+//     second 32 more.
 template <int G>
 __global__ __launch_bounds__(GV8_WAVES * 64, 2) void w8a16_gemv_kernel(
     const uint16_t *__restrict__ x, int M, const int8_t *__restrict__ q8,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ bias, int N, int K,
     uint16_t *__restrict__ y) {
-    constexpr int SPG = G / 32;                  // slices per group
+    constexpr bool PAIR = G == 32;               // two groups per slice
+    constexpr int SPG = PAIR ? 1 : G / 64;       // slices per unit (group, or group pair)
+    static_assert(GV8_DEPTH % SPG == 0, "slot d holds slices t with t % SPG == d % SPG");
     __shared__ float red[GV8_WAVES][16][17];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nl = lane & 15, kb = lane >> 4;
     const int n0 = blockIdx.x * 16;
     const int ncol = min(16, N - n0);
-    const int nslices = K / 32;
     const int ngroups = K / G;
+    const int nunits = PAIR ? ngroups / 2 : ngroups;   // K % 64 == 0
     const int mrow = nl < M ? nl : M - 1;
     // buffer resources: rows past N and slices past K read 0
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -316,52 +335,92 @@ __global__ __launch_bounds__(GV8_WAVES * 64, 2) void w8a16_gemv_kernel(
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(scales + static_cast<int64_t>(n0) * ngroups), 0,
         ncol * ngroups * 2, 0x00020000);
-    const int xo = (mrow * K + 8 * kb) * 2;
-    const int wo = nl * K + 8 * kb;
+    // x pieces of the two MFMAs, byte offsets in the row
+    const int xk0 = PAIR ? 16 * (kb & 1) + 8 * (kb >> 1) : 16 * kb;
+    const int xk1 = PAIR ? xk0 + 32 : xk0 + 8;
+    const int xo = (mrow * K) * 2;
+    const int wo = nl * K + 16 * kb;
     const int so = nl * ngroups * 2;
     constexpr int OOB = 0x40000000;
 
-    // a wave's slices, SPG at a time (one group): j = (wave + 8 i) * SPG ...
-    const int ngrp_w = (ngroups - wave + GV8_WAVES - 1) / GV8_WAVES;   // groups of this wave
+    // a wave's slices, SPG at a time (one unit): j = (wave + 8 i) * SPG ...
+    const int nun_w = (nunits - wave + GV8_WAVES - 1) / GV8_WAVES;   // units of this wave
     const bf16x8 ones = bf16x8_ones();
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
     f32x4 acc = zero4;
-    u32x4 xa[GV8_DEPTH];
-    u32x2 wb[GV8_DEPTH];
-    uint32_t sr[GV8_DEPTH];                       // scale of the slice's group
+    u32x4 xa[GV8_DEPTH][2];
+    u32x4 wb[GV8_DEPTH];
+    uint32_t sr[GV8_DEPTH];                       // the unit's scale (two at G = 32)
     // slice t of this wave's sequence -> global slice index
     auto gslice = [&](int t) { return ((wave + GV8_WAVES * (t / SPG)) * SPG) + (t % SPG); };
-    const int nt_w = ngrp_w * SPG;
+    const int nt_w = nun_w * SPG;
     auto load = [&](int t, int slot) {
         const int j = gslice(t);
         const bool live = t < nt_w;
-        xa[slot] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo, live ? j * 64 : OOB, 0);
-        const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                                                      wrs, wo, live ? j * 32 : OOB, 0));
-        wb[slot] = v;
-        sr[slot] = __builtin_amdgcn_raw_buffer_load_b16(srs, so, live ? (j / SPG) * 2 : OOB, 0);
+        const int xs = live ? j * 128 : OOB;
+        xa[slot][0] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 2 * xk0, xs, 0);
+        xa[slot][1] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 2 * xk1, xs, 0);
+        wb[slot] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wo, live ? j * 64 : OOB, 0);
+        // the scale rides with the slice that folds its group
+        if constexpr (PAIR)
+            sr[slot] = __builtin_amdgcn_raw_buffer_load_b32(srs, so, live ? j * 4 : OOB, 0);
+        else if (slot % SPG == SPG - 1)
+            sr[slot] = __builtin_amdgcn_raw_buffer_load_b16(srs, so, live ? (j / SPG) * 2 : OOB, 0);
     };
-#pragma unroll
-    for (int d = 0; d < GV8_DEPTH; ++d) load(d, d);
     f32x4 accg = zero4, xsg = zero4;
-    for (int t0 = 0; t0 < nt_w; t0 += GV8_DEPTH) {
+    auto fold = [&](float sc) {
 #pragma unroll
-        for (int d = 0; d < GV8_DEPTH; ++d) {
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(sc, accg[i], fmaf(-128.0f * sc, xsg[i], acc[i]));
+    };
+    // (issued slot by slot, in the order of the refills, so that the wait
+    // counts at the loop head are the steady-state ones)
+#pragma unroll
+    for (int d = 0; d < GV8_DEPTH; ++d) {
+        load(d, d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // whole rounds of DEPTH slices; slices past nt_w read nothing (zeros,
+    // scale 0) and add 0
+    const int nt_pad = (nt_w + GV8_DEPTH - 1) / GV8_DEPTH * GV8_DEPTH;
+    for (int t0 = 0; t0 < nt_pad; t0 += GV8_DEPTH) {
+        unrolled(std::make_integer_sequence<int, GV8_DEPTH>{}, [&](auto d_c) {
+            constexpr int d = decltype(d_c)::value;
             const int t = t0 + d;
-            if (t >= nt_w) break;                 // uniform
-            const bf16x8 a = as_bf16x8(xa[d]);
-            const bf16x8 b = bytes8_to_bf16x8(wb[d]);
-            const float s = bf16_to_f32(static_cast<uint16_t>(sr[d]));
-            const bool first = (t % SPG) == 0;
-            xsg = mfma16x16x32(a, ones, first ? zero4 : xsg);
-            accg = mfma16x16x32(a, b, first ? zero4 : accg);
-            load(t + GV8_DEPTH, d);               // refills slot d (after its last use)
-            if ((t % SPG) == SPG - 1) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[i] = fmaf(s, accg[i], fmaf(-128.0f * s, xsg[i], acc[i]));
+            const u32x4 a0 = xa[d][0], a1 = xa[d][1], w = wb[d];
+            // the scales leave sr[d] before its refill, so that the ring keeps
+            // its registers (a copy on the loop edge would wait for every load)
+            constexpr bool folds = PAIR || d % SPG == SPG - 1;
+            float s_lo = 0.0f, s_hi = 0.0f;
+            if constexpr (folds) {
+                s_lo = bf16_to_f32(static_cast<uint16_t>(sr[d] & 0xFFFFu));
+                s_hi = bf16_to_f32(static_cast<uint16_t>(sr[d] >> 16));
+                if constexpr (PAIR) asm volatile("" : "+v"(s_lo), "+v"(s_hi));
+                else asm volatile("" : "+v"(s_lo));
             }
-        }
+            if constexpr (PAIR) {
+                const auto p0 = __builtin_amdgcn_permlane32_swap(w.x, w.z, false, false);
+                const auto p1 = __builtin_amdgcn_permlane32_swap(w.y, w.w, false, false);
+                xsg = mfma16x16x32(as_bf16x8(a0), ones, zero4);
+                accg = mfma16x16x32(as_bf16x8(a0), bytes8_to_bf16x8(u32x2{p0[0], p1[0]}), zero4);
+                fold(s_lo);
+                xsg = mfma16x16x32(as_bf16x8(a1), ones, zero4);
+                accg = mfma16x16x32(as_bf16x8(a1), bytes8_to_bf16x8(u32x2{p0[1], p1[1]}), zero4);
+                fold(s_hi);
+                load(t + GV8_DEPTH, d);           // refills slot d (after its last read)
+            } else {
+                constexpr bool first = d % SPG == 0;     // t % SPG (t0 % DEPTH == 0)
+                xsg = mfma16x16x32(as_bf16x8(a0), ones, first ? zero4 : xsg);
+                accg = mfma16x16x32(as_bf16x8(a0), bytes8_to_bf16x8(u32x2{w.x, w.y}),
+                                    first ? zero4 : accg);
+                xsg = mfma16x16x32(as_bf16x8(a1), ones, xsg);
+                accg = mfma16x16x32(as_bf16x8(a1), bytes8_to_bf16x8(u32x2{w.z, w.w}), accg);
+                load(t + GV8_DEPTH, d);
+                if constexpr (folds) fold(s_lo);
+            }
+            // keep the software pipeline as written: the compiler would
+            // otherwise gather the round's loads at its end and wait for all
+            __builtin_amdgcn_sched_barrier(0);
+        });
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[wave][4 * kb + i][nl] = acc[i];
