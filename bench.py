@@ -31,12 +31,19 @@ ROTATE_BYTES = 1 << 30          # rotate weight copies over >= 1 GiB
 CSRC = os.path.join(ROOT, "bit_gemm_quantize_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # device sources each kernel is built from (a change voids its counters)
+# device sources of each kernel (the launch header only declares host
+# functions and is left out)
 KERNEL_SOURCES = {
-    "quantize_kernel": ["quantize.hip", "w4_device.h", "w4_launch.h"],
-    "quantize_kernel_fake": ["quantize.hip", "w4_device.h", "w4_launch.h"],
-    "gemv_split_kernel": ["gemv.hip", "w4_device.h", "w4_launch.h"],
-    "gemm_kernel": ["gemm.hip", "w4_device.h", "w4_launch.h"],
-    "gemm_kernel_ps": ["gemm.hip", "w4_device.h", "w4_launch.h"],
+    "quantize_kernel": ["quantize.hip", "w4_device.h"],
+    "quantize_kernel_fake": ["quantize.hip", "w4_device.h"],
+    "gemv_split_kernel": ["gemv.hip", "w4_device.h"],
+    "gemm_kernel": ["gemm.hip", "w4_device.h"],
+    "gemm_kernel_ps": ["gemm.hip", "w4_device.h"],
+    "quantize8_kernel": ["w8a16.hip", "w4_device.h"],
+    "w8a16_gemv_kernel": ["w8a16.hip", "w4_device.h"],
+    "w8a16_gemm_kernel": ["w8a16.hip", "w4_device.h"],
+    "w4a8_gemm_kernel": ["w4a8.hip", "w4_device.h"],
+    "act_quant_kernel": ["w4a8.hip", "w4_device.h"],
 }
 
 
