@@ -629,7 +629,9 @@ def main():
 
     for comp, kern in (("quantize", "quantize_kernel"), ("fake_quant_g32", "quantize_kernel_fake"),
                        ("gemv_m1", "gemv_split_kernel"), ("gemm_m2048", "gemm_kernel"),
-                       ("gemm_m2048_ps", "gemm_kernel_ps")):
+                       ("gemm_m2048_ps", "gemm_kernel_ps"), ("w8a16_gemv_m1", "w8a16_gemv_kernel"),
+                       ("quantize8_g128", "quantize8_kernel"), ("w8a16_gemm_m2048", "w8a16_gemm_kernel"),
+                       ("w4a8_gemm_m2048_g128", "w4a8_gemm_kernel")):
         if comp in out:
             tr = measured_traffic(kern)
             out[comp]["traffic_bytes_per_launch"] = round(tr["bytes_per_launch"]) if tr else None
