@@ -593,9 +593,22 @@ def main():
         del g
         g = graph_of(torch, [lambda: torch.bitwise_not(a, out=b)])
         ms_not = time_graphs(torch, [g], 20)
+        # read-only stream: a reduction over the same 1 GiB, timed eagerly
+        # (a multi-block reduction clears memory and stays out of graphs)
+        a32 = a.view(torch.float32)
+        for _ in range(3):
+            torch.sum(a32)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            torch.sum(a32)
+        e1.record()
+        torch.cuda.synchronize()
+        ms_rd = e0.elapsed_time(e1) / 10
         out["hbm_reference"] = {"what": "torch device copy of 1 GiB (read + write)",
                                 "GBps": round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1),
-                                "elementwise_GBps": round(2 * (1 << 30) / (ms_not * 1e-3) / 1e9, 1)}
+                                "elementwise_GBps": round(2 * (1 << 30) / (ms_not * 1e-3) / 1e9, 1),
+                                "read_only_GBps": round((1 << 30) / (ms_rd * 1e-3) / 1e9, 1)}
         del a, b, g
 
     # ---- report ------------------------------------------------------------
