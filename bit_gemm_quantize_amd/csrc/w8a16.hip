@@ -350,7 +350,7 @@ __global__ __launch_bounds__(GV8_WAVES * 64, 2) void w8a16_gemv_kernel(
     f32x4 acc = zero4;
     u32x4 xa[GV8_DEPTH][2];
     u32x4 wb[GV8_DEPTH];
-    uint32_t sr[GV8_DEPTH];                       // the unit's scale (two at G = 32)
+    uint32_t sr[GV8_DEPTH] = {};                  // the unit's scale (two at G = 32)
     // slice t of this wave's sequence -> global slice index
     auto gslice = [&](int t) { return ((wave + GV8_WAVES * (t / SPG)) * SPG) + (t % SPG); };
     const int nt_w = nun_w * SPG;
@@ -361,11 +361,15 @@ __global__ __launch_bounds__(GV8_WAVES * 64, 2) void w8a16_gemv_kernel(
         xa[slot][0] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 2 * xk0, xs, 0);
         xa[slot][1] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 2 * xk1, xs, 0);
         wb[slot] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wo, live ? j * 64 : OOB, 0);
-        // the scale rides with the slice that folds its group
-        if constexpr (PAIR)
-            sr[slot] = __builtin_amdgcn_raw_buffer_load_b32(srs, so, live ? j * 4 : OOB, 0);
-        else if (slot % SPG == SPG - 1)
-            sr[slot] = __builtin_amdgcn_raw_buffer_load_b16(srs, so, live ? (j / SPG) * 2 : OOB, 0);
+        // the scale rides with the slice that folds its group; the 16 lanes
+        // of the first row load it (the fold broadcasts it to the others)
+        if constexpr (PAIR) {
+            if (kb == 0)
+                sr[slot] = __builtin_amdgcn_raw_buffer_load_b32(srs, so, live ? j * 4 : OOB, 0);
+        } else if (slot % SPG == SPG - 1) {
+            if (kb == 0)
+                sr[slot] = __builtin_amdgcn_raw_buffer_load_b16(srs, so, live ? (j / SPG) * 2 : OOB, 0);
+        }
     };
     f32x4 accg = zero4, xsg = zero4;
     auto fold = [&](float sc) {
@@ -392,8 +396,12 @@ __global__ __launch_bounds__(GV8_WAVES * 64, 2) void w8a16_gemv_kernel(
             constexpr bool folds = PAIR || d % SPG == SPG - 1;
             float s_lo = 0.0f, s_hi = 0.0f;
             if constexpr (folds) {
-                s_lo = bf16_to_f32(static_cast<uint16_t>(sr[d] & 0xFFFFu));
-                s_hi = bf16_to_f32(static_cast<uint16_t>(sr[d] >> 16));
+                // row 0 -> rows 0, 0, 2, 2 -> all four rows
+                const auto r1 = __builtin_amdgcn_permlane16_swap(sr[d], sr[d], false, false);
+                const auto r2 = __builtin_amdgcn_permlane32_swap(r1[0], r1[0], false, false);
+                const uint32_t sv = r2[0];
+                s_lo = bf16_to_f32(static_cast<uint16_t>(sv & 0xFFFFu));
+                s_hi = bf16_to_f32(static_cast<uint16_t>(sv >> 16));
                 if constexpr (PAIR) asm volatile("" : "+v"(s_lo), "+v"(s_hi));
                 else asm volatile("" : "+v"(s_lo));
             }
