@@ -36,6 +36,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "quantize_kernel": ["quantize.hip", "w4_device.h"],
     "quantize_kernel_fake": ["quantize.hip", "w4_device.h"],
+    "quantize_batch_kernel": ["quantize.hip", "w4_device.h"],
     "gemv_split_kernel": ["gemv.hip", "w4_device.h"],
     "gemm_kernel": ["gemm.hip", "w4_device.h"],
     "gemm_kernel_ps": ["gemm.hip", "w4_device.h"],
@@ -242,6 +243,8 @@ def main():
     step_bytes = sum(quant_bytes(N, K, G) + linear_bytes(1, N, K, G)
                      for N, K in layers.values())
     ms_per_step = None
+    step_per_layer_ms = None
+    qb_ms = None
     q_ms_launch = {}
     if args.only in ("all", "step", "quantize"):
         # one graph per rotating copy: quantize the four layers, then the
@@ -250,8 +253,18 @@ def main():
             for name in names:
                 q_fn(e, name)()
                 l_fn(e, name)()
-        step_graphs = [graph_of(torch, [q_fn(e, n) for n in names] +
-                                [l_fn(e, n) for n in names]) for e in sets]
+        # one quantize launch per layer (reported for comparison), then the
+        # step proper: the four weights quantized in one launch
+        per_layer = [graph_of(torch, [q_fn(e, n) for n in names] + [l_fn(e, n) for n in names])
+                     for e in sets]
+        step_per_layer_ms = time_graphs(torch, per_layer, max(args.steps, 2))
+        del per_layer
+
+        def qbatch(e):
+            return lambda: w4.quantize_int4_grouped_batch(
+                [e[n][0] for n in names], G, outs=[(e[n][2], e[n][3], e[n][4]) for n in names])
+
+        step_graphs = [graph_of(torch, [qbatch(e)] + [l_fn(e, n) for n in names]) for e in sets]
         log(f"step: warmup {args.warmup}, timed {args.steps} (graph replays)")
         for i in range(args.warmup):
             step_graphs[i % n_sets].replay()
@@ -268,6 +281,19 @@ def main():
         ms_per_step = e0.elapsed_time(e1) / args.steps
         log(f"step: {ms_per_step:.4f} ms (events), {wall_ms:.4f} ms (host clock)")
         del step_graphs
+
+        # the batched quantizer alone: one graph of n_sets launches
+        g = graph_of(torch, [qbatch(e) for e in sets])
+        qb_ms = time_graphs(torch, [g], max(2, reps // n_sets)) / n_sets
+        del g
+        qb_bytes = sum(quant_bytes(N, K, G) for N, K in layers.values())
+        out["quantize_batch"] = {
+            "kernel": "quantize_batch_kernel<128>", "bound": "hbm",
+            "launches_per_step": 1, "avg_launch_us": round(qb_ms * 1e3, 3),
+            "achieved_GBps": round(qb_bytes / (qb_ms * 1e-3) / 1e9, 1),
+            "frac": round(qb_bytes / (qb_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_launch": qb_bytes,
+        }
 
         # the quantizer alone, per layer: one graph of n_sets launches
         per = {}
@@ -617,13 +643,14 @@ def main():
     if ms_per_step is not None:
         value = step_bytes / (ms_per_step * 1e-3) / 1e9
         # dominant kernel of the step: the one with the larger share of time
-        q_ms = sum(q_ms_launch.values())
+        # (the step quantizes the four weights in one batched launch)
+        q_ms = qb_ms
         g_ms = sum(g_ms_launch.values()) if g_ms_launch else 0.0
         if q_ms >= g_ms:
             b = sum(quant_bytes(N, K, G) for N, K in layers.values())
             a_gbs = b / (q_ms * 1e-3) / 1e9
-            kname, klabel = "quantize_kernel", "quantize_kernel<128, false>"
-            nl = len(q_ms_launch)
+            kname, klabel = "quantize_batch_kernel", "quantize_batch_kernel<128>"
+            nl = 1
         else:
             b = sum(linear_bytes(1, N, K, G) for N, K in layers.values())
             a_gbs = b / (g_ms * 1e-3) / 1e9
@@ -641,6 +668,7 @@ def main():
                     "bytes_per_launch_avg": b // nl}
 
     for comp, kern in (("quantize", "quantize_kernel"), ("fake_quant_g32", "quantize_kernel_fake"),
+                       ("quantize_batch", "quantize_batch_kernel"),
                        ("gemv_m1", "gemv_split_kernel"), ("gemm_m2048", "gemm_kernel"),
                        ("gemm_m2048_ps", "gemm_kernel_ps"), ("w8a16_gemv_m1", "w8a16_gemv_kernel"),
                        ("quantize8_g128", "quantize8_kernel"), ("w8a16_gemm_m2048", "w8a16_gemm_kernel"),
@@ -671,8 +699,10 @@ def main():
             "workload": "llama3_8b_decode_layer_set_m1_g128",
             "layers": {k: list(v) for k, v in layers.items()},
             "M": 1, "G": G,
-            "step": "quantize each layer's bf16 weight, then y = x . w_hat^T (M=1); "
-                    "one HIP graph replay per step",
+            "step": "quantize the four bf16 weights (one batched launch), then "
+                    "y = x . w_hat^T per layer (M=1); one HIP graph replay per step",
+            "ms_per_step_one_quantize_launch_per_layer":
+                round(step_per_layer_ms, 5) if step_per_layer_ms is not None else None,
             "step_bytes": step_bytes,
             "rotating_copies": n_sets,
         },

@@ -17,7 +17,7 @@ from .build import LIB_PATH
 __all__ = [
     "W4Status", "W4Path", "W4Error", "GROUP_SIZES", "GEMV_MAX_M", "lib",
     "repack_int4_preshuffled", "w4a16_linear_preshuffled", "quantize_act_int8", "w4a8_linear",
-    "quantize_int8_grouped", "w8a16_linear",
+    "quantize_int8_grouped", "w8a16_linear", "quantize_int4_grouped_batch",
     "quantize_int4_grouped", "fake_quant_int4_grouped", "w4a16_linear", "status_string",
 ]
 
@@ -50,6 +50,14 @@ class W4Error(RuntimeError):
 
 _LIB = None
 _p, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+
+QUANT_BATCH_MAX = 8   # W4_QUANT_BATCH_MAX
+
+
+class QuantJob(ctypes.Structure):
+    """w4_quant_job: one weight of quantize_int4_grouped_batch."""
+    _fields_ = [("W", _p), ("N", _i64), ("K", _i64), ("codes", _p), ("scales", _p),
+                ("zeros", _p)]
 
 
 def lib() -> ctypes.CDLL:
@@ -85,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.quantize_int8_grouped.restype = _int
         L.w8a16_linear.argtypes = [_p, _i64, _p, _p, _p, _i64, _i64, _i64, _p, _p]
         L.w8a16_linear.restype = _int
+        L.quantize_int4_grouped_batch.argtypes = [ctypes.POINTER(QuantJob), _i64, _i64, _p]
+        L.quantize_int4_grouped_batch.restype = _int
         L.w4_status_string.argtypes = [_int]
         L.w4_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -148,6 +158,42 @@ def quantize_int4_grouped(W, G: int, codes=None, scales=None, zeros=None):
     if st != W4Status.OK:
         raise W4Error(st, "quantize_int4_grouped")
     return codes, scales, zeros
+
+
+def quantize_int4_grouped_batch(weights, G: int, outs=None):
+    """quantize_int4_grouped on several bf16 GPU weights in one launch (same
+    G). Returns [(codes, scales, zeros), ...]; ``outs`` (same form) are used
+    when given. Bit-identical to one call per weight."""
+    torch = _torch()
+    weights = list(weights)
+    if not 1 <= len(weights) <= QUANT_BATCH_MAX:
+        raise ValueError(f"1..{QUANT_BATCH_MAX} weights per batch")
+    if outs is None:
+        outs = [None] * len(weights)
+    jobs = (QuantJob * len(weights))()
+    result = []
+    for i, (W, o) in enumerate(zip(weights, outs)):
+        if W.dim() != 2:
+            raise ValueError("each W must be 2-D [N, K]")
+        N, K = W.shape
+        _check(W, "W", torch.bfloat16, (N, K), weights[0].device)
+        ng = K // G if G else 0
+        if o is None:
+            o = (torch.empty((N, K // 2), dtype=torch.uint8, device=W.device),
+                 torch.empty((N, ng), dtype=torch.bfloat16, device=W.device),
+                 torch.empty((N, ng), dtype=torch.bfloat16, device=W.device))
+        codes, scales, zeros = o
+        _check(codes, "codes", torch.uint8, (N, K // 2), W.device)
+        _check(scales, "scales", torch.bfloat16, (N, ng), W.device)
+        _check(zeros, "zeros", torch.bfloat16, (N, ng), W.device)
+        jobs[i] = QuantJob(W.data_ptr(), N, K, codes.data_ptr(), scales.data_ptr(),
+                           zeros.data_ptr())
+        result.append((codes, scales, zeros))
+    st = lib().quantize_int4_grouped_batch(jobs, len(weights), G,
+                                           _stream_ptr(weights[0].device))
+    if st != W4Status.OK:
+        raise W4Error(st, "quantize_int4_grouped_batch")
+    return result
 
 
 def fake_quant_int4_grouped(W, G: int, out=None):

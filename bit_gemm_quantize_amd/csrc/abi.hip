@@ -190,6 +190,46 @@ w4_status w4a8_linear(const int8_t *x8, const float *sx, int64_t M, const uint8_
     return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
 
+w4_status quantize_int4_grouped_batch(const w4_quant_job *jobs, int64_t njobs, int64_t G,
+                                      hipStream_t stream) {
+    if (!jobs) return W4_ERR_NULL;
+    if (njobs < 1 || njobs > W4_QUANT_BATCH_MAX) return W4_ERR_SHAPE;
+    if (!valid_group(G)) return W4_ERR_GROUP;
+    for (int64_t j = 0; j < njobs; ++j) {
+        const w4_quant_job &q = jobs[j];
+        if (!q.W || !q.codes || !q.scales || !q.zeros) return W4_ERR_NULL;
+        const w4_status st = check_nkg(q.N, q.K, G);
+        if (st != W4_OK) return st;
+        if (!aligned16(q.W) || !aligned16(q.codes) || !aligned16(q.scales) || !aligned16(q.zeros))
+            return W4_ERR_ALIGN;
+    }
+    // no output may overlap any input or output of any job
+    for (int64_t j = 0; j < njobs; ++j) {
+        const w4_quant_job &a = jobs[j];
+        const int64_t cb = a.N * a.K / 2, gb = 2 * a.N * (a.K / G);
+        const void *outs[3] = {a.codes, a.scales, a.zeros};
+        const int64_t osz[3] = {cb, gb, gb};
+        for (int64_t i = 0; i < njobs; ++i) {
+            const w4_quant_job &b = jobs[i];
+            const int64_t cbi = b.N * b.K / 2, gbi = 2 * b.N * (b.K / G);
+            for (int o = 0; o < 3; ++o) {
+                if (overlap(outs[o], osz[o], b.W, 2 * b.N * b.K)) return W4_ERR_ALIAS;
+                if (i == j) continue;
+                if (overlap(outs[o], osz[o], b.codes, cbi) ||
+                    overlap(outs[o], osz[o], b.scales, gbi) ||
+                    overlap(outs[o], osz[o], b.zeros, gbi))
+                    return W4_ERR_ALIAS;
+            }
+        }
+        if (overlap(a.codes, cb, a.scales, gb) || overlap(a.codes, cb, a.zeros, gb) ||
+            overlap(a.scales, gb, a.zeros, gb))
+            return W4_ERR_ALIAS;
+    }
+    const hipError_t e = w4::launch_quantize_batch(jobs, static_cast<int>(njobs),
+                                                   static_cast<int>(G), stream);
+    return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+}
+
 w4_status quantize_int8_grouped(const uint16_t *W, int64_t N, int64_t K, int64_t G,
                                 int8_t *codes8, uint16_t *scales, hipStream_t stream) {
     if (!W || !codes8 || !scales) return W4_ERR_NULL;

@@ -230,7 +230,99 @@ __global__ __launch_bounds__(QT_THREADS) void quantize_kernel(
     }
 }
 
+// Several weights in one launch (the layers of a block): the wave chunks of
+// all jobs form one index space, job j owning chunks first[j] ..
+// first[j + 1] - 1; a wave looks its chunk's job up (wave-uniform) and
+// works as quantize_kernel does.
+struct QuantBatch {
+    const u32x4 *W[W4_QUANT_BATCH_MAX];
+    uint32_t *codes[W4_QUANT_BATCH_MAX];
+    uint16_t *scales[W4_QUANT_BATCH_MAX];
+    uint16_t *zeros[W4_QUANT_BATCH_MAX];
+    int64_t npiece[W4_QUANT_BATCH_MAX];
+    int64_t first[W4_QUANT_BATCH_MAX + 1];
+    int njobs;
+};
+
+template <int G>
+__global__ __launch_bounds__(QT_THREADS) void quantize_batch_kernel(const QuantBatch b) {
+    constexpr int WPB = QT_THREADS / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t nw = b.first[b.njobs];
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * WPB;
+    int64_t w = static_cast<int64_t>(blockIdx.x) * WPB +
+                __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    if (w >= nw) return;                       // whole waves
+    auto job_of = [&](int64_t wi) {
+        int j = 0;
+#pragma unroll
+        for (int i = 1; i < W4_QUANT_BATCH_MAX; ++i)
+            if (i < b.njobs && wi >= b.first[i]) j = i;
+        return j;
+    };
+    u32x4 a0, a1, b0, b1;
+    auto load = [&](u32x4 &d0, u32x4 &d1, int64_t wi) {
+        const int64_t wl = wi < nw ? wi : nw - 1;
+        const int j = job_of(wl);
+        const int64_t np = b.npiece[j];
+        const int64_t p0 = 128 * (wl - b.first[j]) + lane, p1 = p0 + 64;
+        d0 = __builtin_nontemporal_load(b.W[j] + (p0 < np ? p0 : np - 1));
+        d1 = __builtin_nontemporal_load(b.W[j] + (p1 < np ? p1 : np - 1));
+    };
+    auto work = [&](const u32x4 &d0, const u32x4 &d1, int64_t wi) {
+        const int j = job_of(wi);
+        const int64_t np = b.npiece[j];
+        const int64_t p0 = 128 * (wi - b.first[j]) + lane, p1 = p0 + 64;
+        quantize8<G, false>(d0, 8 * p0, p0 < np, b.codes[j], b.scales[j], b.zeros[j], nullptr);
+        quantize8<G, false>(d1, 8 * p1, p1 < np, b.codes[j], b.scales[j], b.zeros[j], nullptr);
+    };
+    load(a0, a1, w);
+    int64_t w1 = w + stride;
+    load(b0, b1, w1);
+    work(a0, a1, w);
+    while (w1 < nw) {
+        const int64_t w2 = w1 + stride;
+        load(a0, a1, w2);
+        work(b0, b1, w1);
+        if (w2 >= nw) break;
+        w1 = w2 + stride;
+        load(b0, b1, w1);
+        work(a0, a1, w2);
+    }
+}
+
 } // namespace
+
+hipError_t launch_quantize_batch(const w4_quant_job *jobs, int njobs, int G,
+                                 hipStream_t stream) {
+    QuantBatch b = {};
+    b.njobs = njobs;
+    b.first[0] = 0;
+    for (int j = 0; j < njobs; ++j) {
+        const int64_t nelem = jobs[j].N * jobs[j].K;
+        b.W[j] = reinterpret_cast<const u32x4 *>(jobs[j].W);
+        b.codes[j] = reinterpret_cast<uint32_t *>(jobs[j].codes);
+        b.scales[j] = jobs[j].scales;
+        b.zeros[j] = jobs[j].zeros;
+        b.npiece[j] = nelem / 8;
+        b.first[j + 1] = b.first[j] + (nelem + 1023) / 1024;
+    }
+    for (int j = njobs; j < W4_QUANT_BATCH_MAX; ++j) b.first[j + 1] = b.first[njobs];
+    const int64_t nw = b.first[njobs];
+    constexpr int64_t WPB = QT_THREADS / 64;
+    int64_t blocks = (nw + WPB * QT_UNROLL - 1) / (WPB * QT_UNROLL);
+    const int64_t max_blocks = 256 * 8;        // 8 blocks per compute unit
+    if (blocks > max_blocks) blocks = max_blocks;
+    if (blocks < 1) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(QT_THREADS);
+    switch (G) {
+    case 32: quantize_batch_kernel<32><<<grid, block, 0, stream>>>(b); break;
+    case 64: quantize_batch_kernel<64><<<grid, block, 0, stream>>>(b); break;
+    case 128: quantize_batch_kernel<128><<<grid, block, 0, stream>>>(b); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 namespace {
 

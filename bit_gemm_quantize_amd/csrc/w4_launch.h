@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "w4a16.h"
+
 namespace w4 {
 
 // Compute units of the current device, and the LDS one workgroup may use
@@ -15,6 +17,10 @@ size_t max_lds_per_block();
 hipError_t launch_quantize(const uint16_t *W, int64_t N, int64_t K, int G,
                            uint8_t *codes, uint16_t *scales, uint16_t *zeros,
                            hipStream_t stream);
+
+// Several quantize jobs (same G) in one launch; jobs validated by the caller.
+hipError_t launch_quantize_batch(const w4_quant_job *jobs, int njobs, int G,
+                                 hipStream_t stream);
 
 // Quantize -> dequantize round trip of launch_quantize, bf16 out.
 hipError_t launch_fake_quant(const uint16_t *W, int64_t N, int64_t K, int G, uint16_t *what,

@@ -266,6 +266,30 @@ w4_status w8a16_linear(const uint16_t *x, int64_t M, const int8_t *codes8,
                        const uint16_t *scales, const uint16_t *bias, int64_t N, int64_t K,
                        int64_t G, uint16_t *y, hipStream_t stream);
 
+/*
+ * quantize_int4_grouped_batch - quantize_int4_grouped on several weights in
+ * one launch (e.g. the layers of a transformer block), all with the same G.
+ * Results are bit-identical to one quantize_int4_grouped call per job.
+ *
+ * jobs   in  HOST array of njobs descriptors (read during the call only);
+ *            each job's pointers and shapes follow quantize_int4_grouped
+ * njobs  in  1 <= njobs <= W4_QUANT_BATCH_MAX
+ * Errors: as quantize_int4_grouped for any job (nothing is launched then),
+ * W4_ERR_SHAPE for njobs out of range, W4_ERR_ALIAS when an output overlaps
+ * any input or output of any job.
+ */
+#define W4_QUANT_BATCH_MAX 8
+typedef struct {
+    const uint16_t *W;   /* bf16 [N, K] */
+    int64_t N, K;
+    uint8_t *codes;      /* [N, K/2] */
+    uint16_t *scales;    /* bf16 [N, K/G] */
+    uint16_t *zeros;     /* bf16 [N, K/G] */
+} w4_quant_job;
+
+w4_status quantize_int4_grouped_batch(const w4_quant_job *jobs, int64_t njobs, int64_t G,
+                                      hipStream_t stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char *w4_status_string(int status);
 

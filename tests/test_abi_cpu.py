@@ -33,7 +33,8 @@ def test_header_declares_expected_entry_points():
         "quantize_int4_grouped", "fake_quant_int4_grouped", "w4a16_linear",
         "w4a16_linear_select", "repack_int4_preshuffled", "w4a16_linear_preshuffled",
         "w4a16_linear_preshuffled_select", "quantize_act_int8", "w4a8_linear",
-        "quantize_int8_grouped", "w8a16_linear", "w4_status_string"])
+        "quantize_int8_grouped", "w8a16_linear", "quantize_int4_grouped_batch",
+        "w4_status_string"])
 
 
 def test_library_exports_every_declared_function(L):
@@ -269,6 +270,54 @@ def l8(L, x=A, M=4, codes=B, s=C, bias=None, N=64, K=128, G=32, y=E):
 ])
 def test_w8a16_validation(L, kw, expect):
     assert l8(L, **kw) == expect
+
+
+def qb(L, jobs, n=None, G=32):
+    arr = (w4.QuantJob * max(1, len(jobs)))(*jobs)
+    return L.quantize_int4_grouped_batch(arr, len(jobs) if n is None else n, G, None)
+
+
+def _job(base, N=16, K=128):
+    # W, then codes, scales, zeros laid out apart from each other
+    return w4.QuantJob(base, N, K, base + (1 << 28), base + (1 << 29), base + (3 << 28))
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_array", w4.W4Status.ERR_NULL),
+    ("zero_jobs", w4.W4Status.ERR_SHAPE),
+    ("too_many", w4.W4Status.ERR_SHAPE),
+    ("bad_group", w4.W4Status.ERR_GROUP),
+    ("null_member", w4.W4Status.ERR_NULL),
+    ("bad_shape", w4.W4Status.ERR_SHAPE),
+    ("misaligned", w4.W4Status.ERR_ALIGN),
+    ("codes_over_other_W", w4.W4Status.ERR_ALIAS),
+    ("codes_over_other_codes", w4.W4Status.ERR_ALIAS),
+])
+def test_quantize_batch_validation(L, case, expect):
+    a, b = _job(A), _job(B)
+    if case == "null_array":
+        assert L.quantize_int4_grouped_batch(None, 1, 32, None) == expect
+        return
+    if case == "zero_jobs":
+        assert qb(L, [a], n=0) == expect
+        return
+    if case == "too_many":
+        assert qb(L, [_job(A + (i << 32)) for i in range(9)]) == expect
+        return
+    if case == "bad_group":
+        assert qb(L, [a, b], G=48) == expect
+        return
+    if case == "null_member":
+        b.zeros = None
+    elif case == "bad_shape":
+        b.K = 100                                # K % G != 0
+    elif case == "misaligned":
+        b.scales = b.scales + 8
+    elif case == "codes_over_other_W":
+        b.codes = A + 64
+    elif case == "codes_over_other_codes":
+        b.codes = a.codes
+    assert qb(L, [a, b]) == expect
 
 
 def test_binding_rejects_host_tensors():

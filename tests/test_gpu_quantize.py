@@ -146,3 +146,37 @@ def test_quantize_deterministic(w4):
     b = gu.gpu_quantize(w4, W, 64, guarded=False)
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_quantize_batch_matches_oracle(w4, G):
+    """Several weights in one launch: each job's codes, scales and zeros
+    bit-exact against the oracle (ragged rows, different K, a job smaller
+    than one wave chunk)."""
+    import torch
+    shapes = [(300, 1024), (7, 4 * G), (1, G), (129, 3 * 512), (64, 2048 + G)]
+    Ws = [workloads.random_bf16(s, 0.02, 97 * G + i) for i, s in enumerate(shapes)]
+    Ws[1][0, :G] = 0                                  # a constant group
+    outs = [(gu.Guarded((N, K // 2), torch.uint8), gu.Guarded((N, K // G), torch.bfloat16),
+             gu.Guarded((N, K // G), torch.bfloat16)) for N, K in shapes]
+    gu.log(f"quantize batch G={G} shapes={shapes}")
+    w4.quantize_int4_grouped_batch([gu.to_dev_bf16(W) for W in Ws], G,
+                                   outs=[tuple(b.tensor for b in o) for o in outs])
+    torch.cuda.synchronize()
+    for (N, K), W, o in zip(shapes, Ws, outs):
+        for b in o:
+            b.check_guards()
+        got = (o[0].tensor.cpu().numpy(), gu.to_host_bits(o[1].tensor), gu.to_host_bits(o[2].tensor))
+        gu.assert_quant_equal(got, oracle.quantize_ref(W, G), f"batch job {N}x{K} G={G}")
+
+
+def test_quantize_batch_llama3_8b_set(w4):
+    """The four Llama-3-8B decode layers in one launch equal four single calls."""
+    import torch
+    Ws = [gu.to_dev_bf16(workloads.weight_bits(2, layer)) for layer in workloads.LLAMA3_8B]
+    gu.log("quantize batch llama3-8b set")
+    batch = w4.quantize_int4_grouped_batch(Ws, 128)
+    single = [w4.quantize_int4_grouped(W, 128) for W in Ws]
+    torch.cuda.synchronize()
+    for (cb, sb, zb), (cs, ss, zs) in zip(batch, single):
+        assert torch.equal(cb, cs) and torch.equal(sb, ss) and torch.equal(zb, zs)
