@@ -311,7 +311,9 @@ hipError_t launch_quantize_batch(const w4_quant_job *jobs, int njobs, int G,
     const int64_t nw = b.first[njobs];
     constexpr int64_t WPB = QT_THREADS / 64;
     int64_t blocks = (nw + WPB * QT_UNROLL - 1) / (WPB * QT_UNROLL);
-    const int64_t max_blocks = 256 * 8;        // 8 blocks per compute unit
+    // 24 blocks per compute unit (more than stay resident: finer-grained
+    // work toward the end of the launch; 8 per unit measured ≈ 10% slower)
+    const int64_t max_blocks = static_cast<int64_t>(compute_units()) * 24;
     if (blocks > max_blocks) blocks = max_blocks;
     if (blocks < 1) return hipSuccess;
     const dim3 grid(static_cast<unsigned>(blocks)), block(QT_THREADS);
@@ -333,7 +335,9 @@ hipError_t launch_q(const uint16_t *W, int64_t N, int64_t K, int G, uint8_t *cod
     const int64_t nw = (nelem + 1023) / 1024;  // wave chunks
     constexpr int64_t WPB = QT_THREADS / 64;
     int64_t blocks = (nw + WPB * QT_UNROLL - 1) / (WPB * QT_UNROLL);
-    const int64_t max_blocks = 256 * 8;        // 8 blocks per compute unit
+    // 24 blocks per compute unit (more than stay resident: finer-grained
+    // work toward the end of the launch; 8 per unit measured ≈ 10% slower)
+    const int64_t max_blocks = static_cast<int64_t>(compute_units()) * 24;
     if (blocks > max_blocks) blocks = max_blocks;
     const dim3 grid(static_cast<unsigned>(blocks)), block(QT_THREADS);
     const u32x4 *w4p = reinterpret_cast<const u32x4 *>(W);

@@ -452,7 +452,7 @@ hipError_t launch_quantize8(const uint16_t *W, int64_t N, int64_t K, int G, int8
                             uint16_t *scales, hipStream_t stream) {
     const int64_t nchunk = N * K / 16;
     const int64_t want = (nchunk + Q8_THREADS - 1) / Q8_THREADS;
-    const int64_t cap = static_cast<int64_t>(compute_units()) * 8;
+    const int64_t cap = static_cast<int64_t>(compute_units()) * 24;   // as the int4 quantizer
     const dim3 grid(static_cast<unsigned>(want < cap ? want : cap));
     switch (G) {
     case 32: quantize8_kernel<32><<<grid, dim3(Q8_THREADS), 0, stream>>>(W, nchunk, q8, scales); break;
