@@ -47,7 +47,7 @@ w4_status linear_impl(const uint16_t *x, int64_t M, const uint8_t *codes,
     if (M * K > kMaxElems || M * N > kMaxElems) return W4_ERR_SHAPE;
     if (path != W4_PATH_AUTO && path != W4_PATH_GEMV && path != W4_PATH_GEMM)
         return W4_ERR_PATH;
-    if (path == W4_PATH_GEMV && M > W4_GEMV_MAX_M) return W4_ERR_PATH;
+    if (path == W4_PATH_GEMV && (M > W4_GEMV_MAX_M || K > W4_GEMV_MAX_K)) return W4_ERR_PATH;
     if (!aligned16(codes) || (bias && !aligned16(bias))) return W4_ERR_ALIGN;
     if (pk ? !aligned16(sz) : (!aligned16(scales) || !aligned16(zeros))) return W4_ERR_ALIGN;
     if (M > 0 && (!aligned16(x) || !aligned16(y))) return W4_ERR_ALIGN;
@@ -58,7 +58,8 @@ w4_status linear_impl(const uint16_t *x, int64_t M, const uint8_t *codes,
         overlap(y, ybytes, sz, 2 * gbytes) || overlap(y, ybytes, bias, 2 * N))
         return W4_ERR_ALIAS;
 
-    const bool gemv = path == W4_PATH_GEMV || (path == W4_PATH_AUTO && M <= W4_GEMV_MAX_M);
+    const bool gemv = path == W4_PATH_GEMV ||
+                      (path == W4_PATH_AUTO && M <= W4_GEMV_MAX_M && K <= W4_GEMV_MAX_K);
     const hipError_t e =
         gemv ? w4::launch_gemv(x, static_cast<int>(M), codes, scales, zeros, sz, bias, N, K,
                                static_cast<int>(G), y, stream)

@@ -25,6 +25,8 @@
 //     with xsum_g = sum_{k in g} x[m][k] staged beside x (split kernel) or
 //     from a second MFMA against an all-ones B (phased kernel).
 
+#include <atomic>
+
 #include "w4_device.h"
 #include "w4_launch.h"
 
@@ -882,6 +884,215 @@ __global__ __launch_bounds__(GV_SPLIT_WAVES * 64, 2) void gemv_direct_kernel(
 }
 
 
+constexpr int kMaxDevices = 64;
+
+// Lets `kern` use up to the device's LDS limit as dynamic LDS (the default
+// cap is lower); set once per device and kernel.
+template <typename Kern>
+hipError_t allow_large_lds(Kern kern) {
+    static std::atomic<unsigned long long> done{0};    // bit per device
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    const unsigned long long bit = (dev >= 0 && dev < kMaxDevices) ? 1ull << dev : 0;
+    if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(max_lds_per_block()));
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_relaxed);
+    return e;
+}
+
+// ------------------------------------------------------------------ M = 1
+// Decode GEMV for a single activation row, with the products on the vector
+// ALUs (bf16 pair dot products accumulated in float32). At M = 1 the
+// matrix-core layout above carries 15 padding rows and ties each load to 16
+// rows x 64 bytes; here a wave takes R consecutive output rows and one
+// 2048-wide K segment, lane l covering k = 2048 s + 32 l .. +32 (16 code
+// bytes), so every load of a row is 1 KB contiguous and the blocks of a
+// launch sweep memory in order. A block holds RG row groups x NSB segment
+// waves; a wave whose row needs more than NSB segments takes every NSB-th.
+//   * x: the lane's 32 values stay in registers for all R rows. Loaded
+//     directly (4 x 16 bytes per lane), or (XLDS) as four contiguous 1 KB
+//     runs passed through a per-wave LDS slab, which pays once the row spans
+//     several segments. Plain codes expand in the interleaved order
+//     (0,4), (1,5), (2,6), (3,7), so x is permuted to match; pre-shuffled
+//     codes expand in natural order.
+//   * per row and lane (its 32 codes lie in one group), in float32:
+//       v += s * sum x (128 + q) + (z - 128 s) * sum x.
+//   * the R partial sums are reduced across the wave with lane swaps and
+//     DPP, then across the segment waves of the row through LDS.
+constexpr int GV1_MAX_WAVES = 16;         // waves per block (1024 threads)
+constexpr int GV1_SEG = 2048;             // k per wave segment
+
+// Sum over the 64 lanes of four row partials; every lane of quarter r ends
+// with row r's sum.
+__device__ __forceinline__ float reduce_rows4(float v0, float v1, float v2, float v3) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v2), false, false);
+    const float u02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v1), __float_as_uint(v3), false, false);
+    const float u13 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(u02), __float_as_uint(u13), false, false);
+    return group_sum<16>(__uint_as_float(c[0]) + __uint_as_float(c[1]));
+}
+
+template <int G, int R, bool XLDS, bool PK>
+__global__ __launch_bounds__(GV1_MAX_WAVES * 64) void gemv1_kernel(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
+    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
+    const uint32_t *__restrict__ sz, const uint16_t *__restrict__ bias, int N, int K,
+    uint16_t *__restrict__ y, int nseg, int nsb, int rg) {
+    static_assert(R % 4 == 0, "rows per wave");
+    // dynamic LDS: partial row sums [waves][R] f32, then (XLDS) 4 KB per wave
+    extern __shared__ __attribute__((aligned(16))) uint8_t g1_smem[];
+    float *red = reinterpret_cast<float *>(g1_smem);
+    uint8_t *g1_slab = g1_smem + GV1_MAX_WAVES * R * 4;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int sw = wave % nsb, rgi = wave / nsb;
+    const int64_t row0 = (static_cast<int64_t>(blockIdx.x) * rg + rgi) * R;
+    const uint32_t rows = static_cast<uint32_t>(max<int64_t>(0, min<int64_t>(R, N - row0)));
+    const uint32_t ngroups = static_cast<uint32_t>(K / G);
+    const uint32_t kh = static_cast<uint32_t>(K) >> 1;
+    constexpr uint32_t OOB = 0x80000000u;   // past every resource: reads 0
+    const __amdgpu_buffer_rsrc_t crs = buf_rsrc(codes + row0 * kh, rows * kh);
+    const __amdgpu_buffer_rsrc_t srs =
+        PK ? buf_rsrc(sz + row0 * ngroups, rows * ngroups * 4)
+           : buf_rsrc(scales + row0 * ngroups, rows * ngroups * 2);
+    const __amdgpu_buffer_rsrc_t zrs = PK ? srs : buf_rsrc(zeros + row0 * ngroups, rows * ngroups * 2);
+    const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(x, static_cast<uint32_t>(K) * 2);
+    const uint32_t ones = 0x3F803F80u;      // bf16 pair (1, 1)
+    const Unpack128 uc = unpack128_consts();
+
+    float v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = 0.f;
+
+    for (int seg = sw; seg < nseg; seg += nsb) {
+        const uint32_t k0 = static_cast<uint32_t>(seg) * GV1_SEG + 32u * lane;
+        const bool ok = k0 < static_cast<uint32_t>(K);
+        // x first (needed first), then the codes, then scales / zero-points
+        u32x4 xv[4];
+        if constexpr (XLDS) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {   // piece p = lane + 64 i of the segment (8 k)
+                const uint32_t kx = static_cast<uint32_t>(seg) * GV1_SEG + 8u * (lane + 64 * i);
+                xv[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                    xrs, kx < static_cast<uint32_t>(K) ? kx * 2 : OOB, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, ok ? (k0 + 8 * i) * 2 : OOB, 0, 0);
+        }
+        u32x4 q[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            q[r] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (k0 >> 1) + r * kh : OOB, 0, 0);
+        uint32_t sv[R], zv[R];
+        const uint32_t g = k0 / G;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if constexpr (PK) {
+                const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(
+                    srs, ok ? (r * ngroups + g) * 4 : OOB, 0, 0);
+                sv[r] = w & 0xFFFFu;
+                zv[r] = w >> 16;
+            } else {
+                const uint32_t so = ok ? (r * ngroups + g) * 2 : OOB;
+                sv[r] = __builtin_amdgcn_raw_buffer_load_b16(srs, so, 0, 0);
+                zv[r] = __builtin_amdgcn_raw_buffer_load_b16(zrs, so, 0, 0);
+            }
+        }
+        if constexpr (XLDS) {
+            // piece p -> slot 4 (p / 4) + ((p % 4) ^ ((p / 16) % 4)): the four
+            // reads below (lane l: pieces 4 l .. 4 l + 3) are conflict-free
+            u32x4 *slab = reinterpret_cast<u32x4 *>(g1_slab) + wave * 256;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int p = lane + 64 * i;
+                slab[4 * (p >> 2) + ((p & 3) ^ ((p >> 4) & 3))] = PK ? xv[i] : interleave8_bf16(xv[i]);
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[i] = slab[4 * lane + (i ^ ((lane >> 2) & 3))];
+        } else if constexpr (!PK) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[i] = interleave8_bf16(xv[i]);
+        }
+        float xs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xs = dot2_bf16(xv[i].x, ones, xs);
+            xs = dot2_bf16(xv[i].y, ones, xs);
+            xs = dot2_bf16(xv[i].z, ones, xs);
+            xs = dot2_bf16(xv[i].w, ones, xs);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t w[4];
+                unpack8_bias128_il(q[r][i], w, uc);   // pairs (q0,q4).. plain, (q0,q1).. pre-shuffled
+                p0 = dot2_bf16(xv[i].x, w[0], p0);
+                p1 = dot2_bf16(xv[i].y, w[1], p1);
+                p0 = dot2_bf16(xv[i].z, w[2], p0);
+                p1 = dot2_bf16(xv[i].w, w[3], p1);
+            }
+            const float s = bf16_to_f32(static_cast<uint16_t>(sv[r]));
+            const float zz = fmaf(-128.0f, s, bf16_to_f32(static_cast<uint16_t>(zv[r])));
+            v[r] = fmaf(s, p0 + p1, fmaf(zz, xs, v[r]));
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; r += 4) {
+        const float t = reduce_rows4(v[r], v[r + 1], v[r + 2], v[r + 3]);
+        if ((lane & 15) == 0) red[wave * R + r + (lane >> 4)] = t;
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < rg * R) {
+        const int rr = t / R, r = t % R;
+        const int64_t row = (static_cast<int64_t>(blockIdx.x) * rg + rr) * R + r;
+        if (row < N) {
+            float sum = 0.f;
+            for (int w = 0; w < nsb; ++w) sum += red[(rr * nsb + w) * R + r];
+            if (bias) sum += bf16_to_f32(bias[row]);
+            y[row] = static_cast<uint16_t>(f32_to_bf16_rne(sum));
+        }
+    }
+}
+
+// M = 1: four rows per wave with x loaded directly while a row spans at
+// most two segments (K <= 4096), eight rows with x through LDS beyond
+// (measured on the Llama-3-8B decode shapes and the 32768-square layer).
+template <int G, bool PK>
+hipError_t launch_gemv1(const uint16_t *x, const uint8_t *codes, const uint16_t *scales,
+                        const uint16_t *zeros, const uint32_t *sz, const uint16_t *bias,
+                        int N, int K, uint16_t *y, hipStream_t stream) {
+    const int nseg = (K + GV1_SEG - 1) / GV1_SEG;
+    const int nsb = nseg < GV1_MAX_WAVES ? nseg : GV1_MAX_WAVES;
+    const int rg = nsb >= 4 ? 1 : 4 / nsb;             // about four waves per block
+    const bool xlds = nseg > 2;
+    const int R = xlds ? 8 : 4;
+    const int64_t rows_per_block = static_cast<int64_t>(rg) * R;
+    const unsigned blocks = static_cast<unsigned>((N + rows_per_block - 1) / rows_per_block);
+    const dim3 block(static_cast<unsigned>(rg * nsb * 64));
+    const size_t red_bytes = static_cast<size_t>(GV1_MAX_WAVES) * R * 4;
+    if (xlds) {
+        const hipError_t e = allow_large_lds(gemv1_kernel<G, 8, true, PK>);
+        if (e != hipSuccess) return e;
+        gemv1_kernel<G, 8, true, PK><<<dim3(blocks), block,
+                                       red_bytes + static_cast<size_t>(rg * nsb) * 4096, stream>>>(
+            x, codes, scales, zeros, sz, bias, N, K, y, nseg, nsb, rg);
+    } else {
+        gemv1_kernel<G, 4, false, PK><<<dim3(blocks), block, red_bytes, stream>>>(
+            x, codes, scales, zeros, sz, bias, N, K, y, nseg, nsb, rg);
+    }
+    return hipGetLastError();
+}
+
 // The split kernel stages x through LDS copies (NAT) from this M on.
 constexpr int GV_NAT_MIN_M = 5;
 
@@ -899,16 +1110,8 @@ hipError_t launch_split_s(const uint16_t *x, int M, const uint8_t *codes,
                           const uint16_t *bias, int N, int K, uint16_t *y,
                           hipStream_t stream) {
     auto kern = gemv_split_kernel<G, S, NAT, PK>;
-    static bool attr_set[64] = {false};         // per device
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 static_cast<int>(max_lds_per_block()));
-        if (e != hipSuccess) return e;
-        if (dev >= 0 && dev < 64) attr_set[dev] = true;
-    }
+    const hipError_t e = allow_large_lds(kern);
+    if (e != hipSuccess) return e;
     const size_t lds = split_lds_bytes(M, K, G);
     // resident blocks per compute unit: LDS (160 KB) and 2 blocks of 8 waves
     int per_cu = static_cast<int>(static_cast<size_t>(GV_SPLIT_MAX_LDS) / lds);
@@ -986,6 +1189,7 @@ hipError_t launch_gemv_g(const uint16_t *x, int M, const uint8_t *codes,
                          const uint16_t *bias, int N, int K, uint16_t *y,
                          hipStream_t stream) {
     const int ntiles = (N + 15) / 16;
+    if (M == 1) return launch_gemv1<G, PK>(x, codes, scales, zeros, sz, bias, N, K, y, stream);
     if (M <= GV_SPLIT_MAX_M && split_lds_bytes(M, K, G) <= max_lds_per_block()) {
         return launch_split<G, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
     }
@@ -998,33 +1202,36 @@ hipError_t launch_gemv_g(const uint16_t *x, int M, const uint8_t *codes,
 
 } // namespace
 
+// Per-device values computed on first use. Threads that race on the first
+// call compute the same value; relaxed atomics keep the reads whole.
 int compute_units() {
-    static int cus[64] = {0};
+    static std::atomic<int> cus[kMaxDevices];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int v = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int v = cus[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             v <= 0)
             v = 256;
-        cus[dev] = v;
+        cus[dev].store(v, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return v;
 }
 
 // LDS a workgroup may use on the current device (160 KB on gfx950).
 size_t max_lds_per_block() {
-    static size_t lds[64] = {0};
+    static std::atomic<int> lds[kMaxDevices];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 64 * 1024;
-    if (lds[dev] == 0) {
-        int v = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 64 * 1024;
+    int v = lds[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
             v <= 0)
             v = 64 * 1024;
-        lds[dev] = static_cast<size_t>(v < GV_SPLIT_MAX_LDS ? v : GV_SPLIT_MAX_LDS);
+        v = v < GV_SPLIT_MAX_LDS ? v : GV_SPLIT_MAX_LDS;
+        lds[dev].store(v, std::memory_order_relaxed);
     }
-    return lds[dev];
+    return static_cast<size_t>(v);
 }
 
 hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *codes,

@@ -146,6 +146,21 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) {
     return __builtin_bit_cast(bf16x8, u);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// c + a.lo * b.lo + a.hi * b.hi for two bf16 pairs, accumulated in float32
+// (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Buffer resource over [p, p + bytes): loads at offsets past `bytes` return 0
+// and fetch nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
+}
+
 // bf16 1.0 in every element.
 __device__ __forceinline__ bf16x8 bf16x8_ones() {
     return as_bf16x8(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);

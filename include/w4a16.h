@@ -71,6 +71,10 @@ typedef enum {
 /* Largest M the decode GEMV serves. */
 #define W4_GEMV_MAX_M 16
 
+/* Largest K the decode GEMV serves (its kernels address one row block with
+ * 32-bit offsets); W4_PATH_AUTO sends larger K to the GEMM. */
+#define W4_GEMV_MAX_K (1 << 24)
+
 /*
  * quantize_int4_grouped - quantize a bf16 weight W[N, K] with group size G
  * along K ("Optimum Quanto", "Design overview / Tensors"; torchao int4
@@ -148,8 +152,8 @@ w4_status w4a16_linear(const uint16_t *x, int64_t M, const uint8_t *codes,
 /*
  * w4a16_linear_select - w4a16_linear with an explicit kernel choice, so both
  * kernels can be exercised at the same M. Same arguments and results as
- * w4a16_linear; returns W4_ERR_PATH if path is W4_PATH_GEMV and M > 16, or
- * if path is not a w4_path value.
+ * w4a16_linear; returns W4_ERR_PATH if path is W4_PATH_GEMV and M > 16 or
+ * K > W4_GEMV_MAX_K, or if path is not a w4_path value.
  */
 w4_status w4a16_linear_select(const uint16_t *x, int64_t M,
                               const uint8_t *codes, const uint16_t *scales,

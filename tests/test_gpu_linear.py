@@ -73,7 +73,12 @@ def test_gemv(w4, G, M, shape):
 # multiple of 128) or stage it in phases (otherwise).
 LONG_K_CASES = [(16, 40, 10240, 32), (16, 40, 10240, 64), (16, 40, 10240, 128),
                 (16, 40, 10016, 32), (16, 40, 10048, 64), (6, 72, 16384, 128),
-                (4, 40, 16512, 128), (2, 24, 32768, 64), (9, 33, 12288, 32)]
+                (4, 40, 16512, 128), (2, 24, 32768, 64), (9, 33, 12288, 32),
+                # M = 1: x through the per-wave LDS slab once a row spans more
+                # than two 2048-wide segments; past 16 segments a wave takes
+                # several (K = 40960: 20 segments)
+                (1, 40, 10240, 32), (1, 19, 10048, 64), (1, 24, 14336, 128),
+                (1, 20, 40960, 64), (1, 9, 6144 + 96, 32)]
 
 
 @pytest.mark.parametrize("M,N,K,G", LONG_K_CASES)
