@@ -1,12 +1,19 @@
 """Benchmark of the W4A16 hot path on one MI355X.
 
-A step is one pass of the whole path over the Llama-3-8B-shaped decode layer
-set (qkv, o, gate_up, down; M = 1, G = 128): quantize each layer's bf16
-weight, then run the M = 1 linear on it. ``value`` is the step's algorithmic
-HBM bytes divided by its time. The same run also measures each kernel on
-its own (decode GEMV over rotating weight copies, the quantizer, and the
-M = 2048 prefill GEMM on the Gemma3-12B-shaped layer set) and times the CPU
-oracle on a bounded sample of the step's work.
+Headline (``value``): the M = 1 W4A16 linear ``y = x . w_hat^T`` over the
+Llama-3-8B-shaped decode layer set (qkv, o, gate_up, down; G = 128), in GB/s
+of algorithmic HBM bytes. A step is one pass over the four layers, run back
+to back as a decode step runs them (one HIP graph replay per step), with
+>= 1 GiB of distinct quantized weight copies rotated so that no cache holds
+the weights. ``roofline`` is the decode GEMV kernel against the 8 TB/s HBM
+peak; ``roofline_prefill`` is the M = 2048 GEMM on the Gemma3-12B-shaped
+layer set against the 2.5 PFLOP/s dense bf16 matrix peak (the metric's second
+half). ``components`` times every other kernel and workload on its own (the
+quantizer, the quantize + linear step, M = 16 decode at G = 32 and 64, the
+32768-square layer, the pre-shuffled layout, W4A8, int8 weight-only) next to
+a plain read-only streaming kernel at the same sizes (the achievable
+ceiling). ``cpu_baseline`` times the CPU oracle on bounded samples of each
+workload.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -14,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -24,19 +32,19 @@ if ROOT not in sys.path:
 
 METRIC = ("W4A16 linear: achieved HBM GB/s (M=1) and TFLOP/s (M=2048), "
           "% of roofline")
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 MFMA_INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 matrix peak
 ROTATE_BYTES = 1 << 30          # rotate weight copies over >= 1 GiB
 CSRC = os.path.join(ROOT, "bit_gemm_quantize_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
-# device sources each kernel is built from (a change voids its counters)
-# device sources of each kernel (the launch header only declares host
-# functions and is left out)
+# device sources each kernel is compiled from (a change voids its counters;
+# the launch header only declares host functions and is left out)
 KERNEL_SOURCES = {
     "quantize_kernel": ["quantize.hip", "w4_device.h"],
     "quantize_kernel_fake": ["quantize.hip", "w4_device.h"],
     "quantize_batch_kernel": ["quantize.hip", "w4_device.h"],
+    "gemv1_kernel": ["gemv.hip", "w4_device.h"],
     "gemv_split_kernel": ["gemv.hip", "w4_device.h"],
     "gemm_kernel": ["gemm.hip", "w4_device.h"],
     "gemm_kernel_ps": ["gemm.hip", "w4_device.h"],
@@ -45,7 +53,10 @@ KERNEL_SOURCES = {
     "w8a16_gemm_kernel": ["w8a16.hip", "w4_device.h"],
     "w4a8_gemm_kernel": ["w4a8.hip", "w4_device.h"],
     "act_quant_kernel": ["w4a8.hip", "w4_device.h"],
+    "read_stream_kernel": ["measure.hip", "w4_device.h"],
 }
+PARTS = ["all", "decode", "gemm", "step", "quantize", "fake", "gemv16", "square", "ps", "w4a8",
+         "w8a16", "stream", "copy"]
 
 
 def log(msg):
@@ -53,10 +64,12 @@ def log(msg):
 
 
 def quant_bytes(N, K, G):
+    """Algorithmic bytes of one quantize pass: read W, write codes, scales, zeros."""
     return 2 * N * K + N * K // 2 + 4 * N * K // G
 
 
 def linear_bytes(M, N, K, G):
+    """Algorithmic bytes of one linear: codes, scales, zeros, x and y once each."""
     return N * K // 2 + 4 * N * K // G + 2 * M * K + 2 * M * N
 
 
@@ -73,9 +86,9 @@ def kernel_source_hash(kernel):
 def measured_traffic(kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this kernel (FETCH_SIZE + WRITE_SIZE, each scaled by the factor the same
-    counter gives for a plain device copy of known size). Returns None when
-    no summary exists or the kernel's sources changed since it was taken.
-    The summary carries one machine-readable line:
+    counter gives for a plain elementwise kernel of known size). None when no
+    summary exists or the kernel's sources changed since it was taken. The
+    summary carries one machine-readable line:
       traffic: kernel=<name> sources_sha256=<hex> fetch_bytes=<B> write_bytes=<B>
     """
     try:
@@ -115,8 +128,9 @@ def graph_of(torch, fns):
 
 
 def time_graphs(torch, graphs, reps, warmup=2):
-    """Replay the graphs round-robin; HIP events around the timed replays on
-    the current stream. Returns milliseconds per replay."""
+    """Replay the graphs round-robin; HIP events on torch's current stream
+    (the stream every launch is enqueued on) around the timed replays.
+    Returns milliseconds per replay."""
     for i in range(warmup * len(graphs)):
         graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
@@ -130,19 +144,183 @@ def time_graphs(torch, graphs, reps, warmup=2):
     return e0.elapsed_time(e1) / reps
 
 
-def make_layer(torch, N, K, seed, M, dev):
+def time_launches(torch, fns, reps):
+    """ms per launch of fns[i % len(fns)]: one graph holding every fn once,
+    replayed ceil(reps / len(fns)) times."""
+    g = graph_of(torch, fns)
+    n = max(2, -(-reps // len(fns)))
+    ms = time_graphs(torch, [g], n) / len(fns)
+    del g
+    return ms
+
+
+def make_weight(torch, N, K, seed, dev, outlier_cols=None):
+    """Seeded synthetic weight on the device: N(0, 0.02) in fp32, cast to bf16
+    (round to nearest even); optional outlier columns scaled x20 first."""
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
-    W = (torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * 0.02
-         ).to(torch.bfloat16)
-    x = torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
-    return W, x
+    W = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * 0.02
+    if outlier_cols is not None:
+        W[:, torch.as_tensor(outlier_cols, device=dev)] *= 20.0
+    return W.to(torch.bfloat16)
 
 
-def cpu_baseline(layers, G, min_s=10.0, max_s=30.0):
-    """Time the CPU oracle (quantize + M = 1 linear) on the decode layer set,
-    on this host's cores: whole layers, cycling through the set until at
-    least min_s of work has been timed (stopping early past max_s)."""
+def make_x(torch, M, K, seed, dev):
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return torch.randn((M, K), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+
+def rate(b, ms):
+    return b / (ms * 1e-3) / 1e9
+
+
+# ------------------------------------------------------------------ decode
+def decode_set(torch, w4, dev, layers, M, G, seed0, reps, ps=False, outliers=False,
+               kernel="", want_step=False, steps=0, warmup=0):
+    """M-row linear on each layer over rotating quantized copies (>= 1 GiB).
+    Returns (component dict, step timing or None)."""
+    import workloads
+    names = list(layers)
+    set_bytes = sum(linear_bytes(M, N, K, G) for N, K in layers.values())
+    n_cp = max(2, -(-ROTATE_BYTES // set_bytes))
+    log(f"decode M={M} G={G}{' pre-shuffled' if ps else ''}: {n_cp} rotating copies "
+        f"of {set_bytes / 1e6:.1f} MB")
+    copies = []
+    for r in range(n_cp):
+        entry = {}
+        for li, (name, (N, K)) in enumerate(layers.items()):
+            oc = workloads.outlier_columns(K, seed0 + li) if outliers else None
+            W = make_weight(torch, N, K, seed0 + 1000 * r + li, dev, oc)
+            c, s_, z = w4.quantize_int4_grouped(W, G)
+            del W
+            if ps:
+                c, s_ = w4.repack_int4_preshuffled(c, s_, z, G)
+                z = None
+            x = make_x(torch, M, K, seed0 + 500 + 1000 * r + li, dev)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            entry[name] = (x, c, s_, z, y)
+        copies.append(entry)
+    torch.cuda.synchronize()
+
+    def fn(e, name):
+        x, c, s_, z, y = e[name]
+        if ps:
+            return lambda: w4.w4a16_linear_preshuffled(x, c, s_, G, out=y)
+        return lambda: w4.w4a16_linear(x, c, s_, z, G, out=y)
+
+    for e in copies:                        # eager warm-up of every launch
+        for name in names:
+            fn(e, name)()
+    per = {}
+    tot_ms = 0.0
+    for name, (N, K) in layers.items():
+        ms = time_launches(torch, [fn(e, name) for e in copies], max(reps, 2 * n_cp))
+        b = linear_bytes(M, N, K, G)
+        per[name] = {"us": round(ms * 1e3, 3), "GBps": round(rate(b, ms), 1), "bytes": b}
+        tot_ms += ms
+    comp = {
+        "kernel": kernel, "bound": "hbm", "M": M, "G": G,
+        "layout": "pre-shuffled" if ps else "plain",
+        "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
+        "achieved_GBps": round(rate(set_bytes, tot_ms), 1),
+        "frac": round(rate(set_bytes, tot_ms) / HBM_PEAK_GBS, 4),
+        "bytes_per_set": set_bytes, "per_layer": per, "rotating_copies": n_cp,
+    }
+    step = None
+    # the four layers back to back, one graph per copy, as a decode step runs them
+    graphs = [graph_of(torch, [fn(e, n) for n in names]) for e in copies]
+    if want_step:
+        log(f"decode step: warmup {warmup}, timed {steps} (graph replays)")
+        for i in range(warmup):
+            graphs[i % n_cp].replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            graphs[i % n_cp].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        step = {"ms": e0.elapsed_time(e1) / steps, "wall_ms": wall_ms, "bytes": set_bytes,
+                "copies": n_cp}
+        comp["set_back_to_back_us"] = round(step["ms"] * 1e3, 3)
+    else:
+        set_ms = time_graphs(torch, graphs, max(2 * n_cp, reps // 2))
+        comp["set_back_to_back_us"] = round(set_ms * 1e3, 3)
+    comp["set_back_to_back_GBps"] = round(rate(set_bytes, comp["set_back_to_back_us"] * 1e-3), 1)
+    del graphs, copies
+    return comp, step
+
+
+def stream_ceiling(torch, w4, dev, sizes, reps):
+    """The plain read-only streaming kernel over each size, rotating through a
+    buffer of >= 1 GiB so that every launch reads distinct bytes."""
+    def plan(b):
+        b16 = b - b % 16
+        step = -(-b16 // 4096) * 4096
+        n = max(2, -(-ROTATE_BYTES // step) + 1)
+        return b16, step, n
+
+    total = max(n * step for _, step, n in (plan(b) for b in sizes.values()))
+    buf = torch.empty(total, dtype=torch.uint8, device=dev)
+    buf.fill_(0x5A)
+    sink = torch.empty(64, dtype=torch.int32, device=dev)
+    out = {}
+    for label, b in sizes.items():
+        b16, step, n = plan(b)
+        offs = [i * step for i in range(n)]
+        fns = [(lambda o=o: w4.read_stream(buf[o:o + b16], b16, sink)) for o in offs]
+        ms = time_launches(torch, fns, max(reps, 2 * n))
+        out[label] = {"us": round(ms * 1e3, 3), "GBps": round(rate(b16, ms), 1), "bytes": b16}
+    del buf
+    return out
+
+
+# ------------------------------------------------------------------- prefill
+def prefill_set(torch, w4, dev, layers, M, G, reps, ps=False, kernel=""):
+    log(f"prefill M={M} G={G}{' pre-shuffled' if ps else ''}: Gemma3-12B-shaped layers")
+    per = {}
+    tot_ms = 0.0
+    tot_f = 0
+    for i, (name, (N, K)) in enumerate(layers.items()):
+        W = make_weight(torch, N, K, 50 + i, dev)
+        c, s_, z = w4.quantize_int4_grouped(W, G)
+        del W
+        if ps:
+            c, s_ = w4.repack_int4_preshuffled(c, s_, z, G)
+            z = None
+        x = make_x(torch, M, K, 550 + i, dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        if ps:
+            fn = (lambda x=x, c=c, s_=s_, y=y: w4.w4a16_linear_preshuffled(x, c, s_, G, out=y))
+        else:
+            fn = (lambda x=x, c=c, s_=s_, z=z, y=y: w4.w4a16_linear(x, c, s_, z, G, out=y))
+        fn()
+        ms = time_launches(torch, [fn], max(3, reps // 5))
+        f = 2 * M * N * K
+        per[name] = {"us": round(ms * 1e3, 2), "TFLOPs": round(f / (ms * 1e-3) / 1e12, 1)}
+        tot_ms += ms
+        tot_f += f
+        del x, c, s_, z, y
+    tf = tot_f / (tot_ms * 1e-3) / 1e12
+    return {"kernel": kernel, "bound": "mfma", "M": M, "G": G,
+            "layout": "pre-shuffled" if ps else "plain",
+            "avg_launch_us": round(tot_ms * 1e3 / len(layers), 2),
+            "achieved_TFLOPs": round(tf, 1), "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "flops_per_set": tot_f, "set_us": round(tot_ms * 1e3, 2), "per_layer": per}
+
+
+# ------------------------------------------------------------------ oracle
+def cpu_baseline(G_dec=128):
+    """The CPU oracle (numpy; the quantizer single-threaded, the fp64 matmul
+    on all BLAS threads) timed on bounded samples of every workload, on this
+    host. The headline figure is the M = 1 linear over the whole decode set in
+    GB/s of the same algorithmic bytes as ``value``."""
+    import numpy as np
+
     import oracle
     import workloads
 
@@ -152,33 +330,96 @@ def cpu_baseline(layers, G, min_s=10.0, max_s=30.0):
                             if i.get("user_api") == "blas"] or [1])
     except Exception:                                   # pragma: no cover
         blas_threads = 1
-    inputs = {name: (workloads.weight_bits(2, name), workloads.activation_bits(2, 1, K))
-              for name, (N, K) in layers.items()}
-    total_bytes = 0
-    t_total = 0.0
-    done = []
-    while t_total < min_s:
+    per = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    # config 1: the 512 x 512 layer, G = 32, one input row
+    W1 = workloads.weight_bits(1, "linear")
+    x1 = workloads.activation_bits(1, 1, 512)
+    (c1, s1, z1), tq = timed(lambda: oracle.quantize_ref(W1, 32))
+    _, tl = timed(lambda: oracle.linear_ref(x1, c1, s1, z1, 32))
+    per["tiny_512_g32"] = {"quantize_ms": round(tq * 1e3, 3), "linear_m1_ms": round(tl * 1e3, 3)}
+
+    # config 2: the decode set, whole layers: quantize once, then the M = 1
+    # linear repeated until >= 6 s of work has been timed
+    layers = dict(workloads.LLAMA3_8B)
+    qs = {}
+    tq_tot = 0.0
+    for name in layers:
+        W = workloads.weight_bits(2, name)
+        qs[name], t = timed(lambda W=W: oracle.quantize_ref(W, G_dec))
+        tq_tot += t
+        del W
+    xs = {name: workloads.activation_bits(2, 1, K) for name, (N, K) in layers.items()}
+    lin_b = 0
+    lin_t = 0.0
+    passes = 0
+    while lin_t < 6.0 and passes < 10:
         for name, (N, K) in layers.items():
-            W, x = inputs[name]
-            t0 = time.perf_counter()
-            c, s, z = oracle.quantize_ref(W, G)
-            oracle.linear_ref(x, c, s, z, G)
-            t_total += time.perf_counter() - t0
-            total_bytes += quant_bytes(N, K, G) + linear_bytes(1, N, K, G)
-            done.append(name)
-            if t_total > max_s:
-                break
-        if t_total > max_s:
-            break
+            c, s_, z = qs[name]
+            _, t = timed(lambda: oracle.linear_ref(xs[name], c, s_, z, G_dec))
+            lin_t += t
+            lin_b += linear_bytes(1, N, K, G_dec)
+        passes += 1
+    qb = sum(quant_bytes(N, K, G_dec) for N, K in layers.values())
+    per["llama3_8b_decode_m1_g128"] = {
+        "linear_GBps": round(lin_b / lin_t / 1e9, 4), "linear_passes": passes,
+        "quantize_GBps": round(qb / tq_tot / 1e9, 4), "quantize_s": round(tq_tot, 2)}
+    headline = lin_b / lin_t / 1e9
+    del qs
+
+    # config 3: M = 16, G = 32 and 64, outlier columns: the o layer
+    N, K = layers["o"]
+    for G in (32, 64):
+        W = workloads.weight_bits(3, "o")
+        x = workloads.activation_bits(3, 16, K)
+        (c, s_, z), tq = timed(lambda: oracle.quantize_ref(W, G))
+        _, tl = timed(lambda: oracle.linear_ref(x, c, s_, z, G))
+        per[f"llama3_8b_m16_g{G}_o"] = {"linear_GBps": round(linear_bytes(16, N, K, G) / tl / 1e9, 4),
+                                         "quantize_GBps": round(quant_bytes(N, K, G) / tq / 1e9, 4)}
+
+    # config 4: M = 2048, G = 128: the k layer (2048 x 3840)
+    N, K = dict(workloads.GEMMA3_12B)["k"]
+    W = workloads.weight_bits(4, "k")
+    x = workloads.activation_bits(4, 2048, K)
+    c, s_, z = oracle.quantize_ref(W, 128)
+    _, tl = timed(lambda: oracle.linear_ref(x, c, s_, z, 128))
+    per["gemma3_12b_prefill_m2048_k"] = {"linear_TFLOPs": round(2 * 2048 * N * K / tl / 1e12, 5)}
+
+    # config 5: 32768 x 32768, G = 64, on 1024 seeded weight rows; the full
+    # size is extrapolated from the sample (labelled so)
+    rows = 1024
+    NS = KS = 32768
+    W = workloads.weight_bits(5, "square", rows=(0, rows))
+    (c, s_, z), tq = timed(lambda: oracle.quantize_ref(W, 64))
+    x1 = workloads.activation_bits(5, 1, KS)
+    _, tl1 = timed(lambda: oracle.linear_ref(x1, c, s_, z, 64))
+    x256 = workloads.activation_bits(5, 256, KS, rows=(0, 256))
+    _, tl256 = timed(lambda: oracle.linear_ref(x256, c, s_, z, 64))
+    scale_n = NS / rows
+    per["square_32768_g64"] = {
+        "sample": f"{rows} of {NS} weight rows (quantize, M=1); 256 of 32768 x rows x "
+                  f"{rows} weight rows (M=32768); full-size times extrapolated",
+        "quantize_s_extrapolated": round(tq * scale_n, 2),
+        "quantize_GBps": round(quant_bytes(rows, KS, 64) / tq / 1e9, 4),
+        "linear_m1_s_extrapolated": round(tl1 * scale_n, 3),
+        "linear_m32768_s_extrapolated": round(tl256 * scale_n * (32768 / 256), 1),
+        "linear_m32768_TFLOPs": round(2 * 256 * rows * KS / tl256 / 1e12, 5)}
+    del W, c, s_, z
+
     return {
-        "value": round(total_bytes / t_total / 1e9, 4),
+        "value": round(headline, 4),
         "unit": "GB/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": ("numpy oracle, quantize (single thread) + float64 M=1 linear "
-                   f"(BLAS, {blas_threads} threads) over whole decode layers "
-                   f"({len(done)} layer passes: {', '.join(done)}); "
-                   f"{total_bytes / 1e6:.1f} MB of algorithmic bytes in {t_total:.2f} s"),
+        "sample": ("numpy oracle: M=1 fp64 linear (BLAS, "
+                   f"{blas_threads} threads) over the four whole decode layers, {passes} passes; "
+                   "per_config: the other workloads on bounded samples (quantizer single-threaded)"),
+        "per_config": per,
         "host_cpus": os.cpu_count(),
         "host_affinity": len(os.sched_getaffinity(0)),
     }
@@ -190,13 +431,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "step", "gemv", "gemv16", "gemm", "quantize", "fake", "ps", "w4a8",
-                                       "w8a16", "copy"],
-                    default="all", help="restrict to one part (for profiling)")
+    ap.add_argument("--only", choices=PARTS, default="all",
+                    help="restrict to one part (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path has no multi-GPU part in this build)", file=sys.stderr)
+              "(the path has no multi-GPU part: every box here has one GPU)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -211,307 +451,214 @@ def main():
     torch.cuda.set_device(dev)
     G = 128
     layers = dict(workloads.LLAMA3_8B)
-    names = list(layers)
+    glayers = dict(workloads.GEMMA3_12B)
     out = {}
     reps = max(args.steps, 1)
+    only = args.only
 
-    # ---- inputs of the step: rotating copies of the decode layer set -----
-    set_bytes = sum(quant_bytes(N, K, G) for N, K in layers.values())
-    n_sets = max(2, -(-ROTATE_BYTES // set_bytes))
-    log(f"decode layer set: {n_sets} rotating copies of {set_bytes / 1e6:.1f} MB")
-    sets = []
-    for r in range(n_sets):
-        entry = {}
-        for i, (name, (N, K)) in enumerate(layers.items()):
-            W, x = make_layer(torch, N, K, 1000 * r + i, 1, dev)
-            codes = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
-            sc = torch.empty((N, K // G), dtype=torch.bfloat16, device=dev)
-            ze = torch.empty((N, K // G), dtype=torch.bfloat16, device=dev)
-            y = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
-            entry[name] = (W, x, codes, sc, ze, y)
-        sets.append(entry)
-    torch.cuda.synchronize()
+    def want(*parts):
+        return only == "all" or only in parts
 
-    def q_fn(e, name):
-        W, x, codes, sc, ze, y = e[name]
-        return lambda: w4.quantize_int4_grouped(W, G, codes, sc, ze)
+    # ---- headline: M = 1 linear over the decode set --------------------------
+    step = None
+    if want("decode"):
+        comp, step = decode_set(
+            torch, w4, dev, layers, 1, G, 0, reps,
+            kernel="gemv1_kernel<128, 4, false, false> (qkv, o, gate_up), "
+                   "gemv1_kernel<128, 8, true, false> (down)",
+            want_step=True, steps=max(args.steps, 1), warmup=args.warmup)
+        out["gemv_m1_g128"] = comp
+    if want("decode", "stream"):
+        sizes = {n: linear_bytes(1, N, K, G) for n, (N, K) in layers.items()}
+        sizes["square_m1"] = linear_bytes(1, 32768, 32768, 64)
+        sizes["1GiB"] = 1 << 30
+        ceil = stream_ceiling(torch, w4, dev, sizes, reps)
+        dec = {k: v for k, v in ceil.items() if k in layers}
+        set_b = sum(v["bytes"] for v in dec.values())
+        set_us = sum(v["us"] for v in dec.values())
+        out["read_stream_ceiling"] = {
+            "kernel": "read_stream_kernel (plain read-only stream, 4 KB per wave)",
+            "per_size": ceil, "decode_set_GBps": round(set_b / (set_us * 1e-6) / 1e9, 1),
+            "decode_set_frac": round(set_b / (set_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
-    def l_fn(e, name):
-        W, x, codes, sc, ze, y = e[name]
-        return lambda: w4.w4a16_linear(x, codes, sc, ze, G, out=y)
+    # ---- the metric's second half: M = 2048 GEMM -----------------------------
+    if want("gemm"):
+        out["gemm_m2048_g128"] = prefill_set(torch, w4, dev, glayers, 2048, G, reps,
+                                             kernel="gemm_kernel<128, false>")
 
-    step_bytes = sum(quant_bytes(N, K, G) + linear_bytes(1, N, K, G)
-                     for N, K in layers.values())
-    ms_per_step = None
-    step_per_layer_ms = None
-    qb_ms = None
-    q_ms_launch = {}
-    if args.only in ("all", "step", "quantize"):
-        # one graph per rotating copy: quantize the four layers, then the
-        # four M = 1 linears on the fresh codes
-        for e in sets:                      # eager warm-up of every launch
-            for name in names:
-                q_fn(e, name)()
-                l_fn(e, name)()
-        # one quantize launch per layer (reported for comparison), then the
-        # step proper: the four weights quantized in one launch
-        per_layer = [graph_of(torch, [q_fn(e, n) for n in names] + [l_fn(e, n) for n in names])
-                     for e in sets]
-        step_per_layer_ms = time_graphs(torch, per_layer, max(args.steps, 2))
-        del per_layer
+    # ---- decode step with the quantizer: quantize the four weights (one
+    # batched launch) then the four M = 1 linears on the fresh codes ----------
+    if want("step", "quantize"):
+        set_qbytes = sum(quant_bytes(N, K, G) for N, K in layers.values())
+        n_sets = max(2, -(-ROTATE_BYTES // set_qbytes))
+        log(f"quantize: {n_sets} rotating copies of {set_qbytes / 1e6:.1f} MB")
+        sets = []
+        for r in range(n_sets):
+            entry = {}
+            for i, (name, (N, K)) in enumerate(layers.items()):
+                W = make_weight(torch, N, K, 1000 * r + i, dev)
+                entry[name] = (W, make_x(torch, 1, K, 7000 + 1000 * r + i, dev),
+                               torch.empty((N, K // 2), dtype=torch.uint8, device=dev),
+                               torch.empty((N, K // G), dtype=torch.bfloat16, device=dev),
+                               torch.empty((N, K // G), dtype=torch.bfloat16, device=dev),
+                               torch.empty((1, N), dtype=torch.bfloat16, device=dev))
+            sets.append(entry)
+        names = list(layers)
 
         def qbatch(e):
             return lambda: w4.quantize_int4_grouped_batch(
                 [e[n][0] for n in names], G, outs=[(e[n][2], e[n][3], e[n][4]) for n in names])
 
-        step_graphs = [graph_of(torch, [qbatch(e)] + [l_fn(e, n) for n in names]) for e in sets]
-        log(f"step: warmup {args.warmup}, timed {args.steps} (graph replays)")
-        for i in range(args.warmup):
-            step_graphs[i % n_sets].replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record()
-        for i in range(args.steps):
-            step_graphs[i % n_sets].replay()
-        e1.record()
-        torch.cuda.synchronize()
-        wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        ms_per_step = e0.elapsed_time(e1) / args.steps
-        log(f"step: {ms_per_step:.4f} ms (events), {wall_ms:.4f} ms (host clock)")
-        del step_graphs
+        def lin(e, n):
+            return lambda: w4.w4a16_linear(e[n][1], e[n][2], e[n][3], e[n][4], G, out=e[n][5])
 
-        # the batched quantizer alone: one graph of n_sets launches
-        g = graph_of(torch, [qbatch(e) for e in sets])
-        qb_ms = time_graphs(torch, [g], max(2, reps // n_sets)) / n_sets
-        del g
-        qb_bytes = sum(quant_bytes(N, K, G) for N, K in layers.values())
-        out["quantize_batch"] = {
+        for e in sets:
+            qbatch(e)()
+            for n in names:
+                lin(e, n)()
+        if want("step"):
+            g = [graph_of(torch, [qbatch(e)] + [lin(e, n) for n in names]) for e in sets]
+            ms = time_graphs(torch, g, max(reps, 2 * n_sets))
+            del g
+            sb = set_qbytes + sum(linear_bytes(1, N, K, G) for N, K in layers.values())
+            out["decode_step_quantize_and_linear"] = {
+                "what": "quantize the four bf16 weights (one batched launch), then the four "
+                        "M=1 linears on the fresh codes; one graph replay",
+                "ms": round(ms, 5), "bytes": sb, "GBps": round(rate(sb, ms), 1)}
+        qb_ms = time_launches(torch, [qbatch(e) for e in sets], max(reps, 2 * n_sets))
+        out["quantize_batch_g128"] = {
             "kernel": "quantize_batch_kernel<128>", "bound": "hbm",
-            "launches_per_step": 1, "avg_launch_us": round(qb_ms * 1e3, 3),
-            "achieved_GBps": round(qb_bytes / (qb_ms * 1e-3) / 1e9, 1),
-            "frac": round(qb_bytes / (qb_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes_per_launch": qb_bytes,
-        }
-
-        # the quantizer alone, per layer: one graph of n_sets launches
+            "avg_launch_us": round(qb_ms * 1e3, 3), "bytes_per_launch": set_qbytes,
+            "achieved_GBps": round(rate(set_qbytes, qb_ms), 1),
+            "frac": round(rate(set_qbytes, qb_ms) / HBM_PEAK_GBS, 4)}
         per = {}
         tot_b = 0
         tot_ms = 0.0
         for name, (N, K) in layers.items():
-            g = graph_of(torch, [q_fn(e, name) for e in sets])
-            ms = time_graphs(torch, [g], max(2, reps // n_sets)) / n_sets
-            q_ms_launch[name] = ms
+            fns = [(lambda e=e, n=name: w4.quantize_int4_grouped(e[n][0], G, e[n][2], e[n][3],
+                                                                 e[n][4])) for e in sets]
+            ms = time_launches(torch, fns, max(reps, 2 * n_sets))
             b = quant_bytes(N, K, G)
-            per[name] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1)}
+            per[name] = {"us": round(ms * 1e3, 3), "GBps": round(rate(b, ms), 1)}
             tot_b += b
             tot_ms += ms
-            del g
-        out["quantize"] = {
+        out["quantize_g128"] = {
             "kernel": "quantize_kernel<128, false>", "bound": "hbm",
             "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
-            "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
-            "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes_per_set": tot_b, "set_us": round(tot_ms * 1e3, 3),
-            "per_layer": per,
-        }
+            "achieved_GBps": round(rate(tot_b, tot_ms), 1),
+            "frac": round(rate(tot_b, tot_ms) / HBM_PEAK_GBS, 4),
+            "bytes_per_set": tot_b, "per_layer": per}
+        del sets
 
-    # ---- fake-quantize round trip (QAT forward weight), G = 32 ------------
-    if args.only in ("all", "fake"):
-        GF = 32
+    # ---- fake-quantize round trip (QAT forward weight), G = 32 ---------------
+    if want("fake"):
         per = {}
         tot_b = 0
         tot_ms = 0.0
-        for name, (N, K) in layers.items():
+        for i, (name, (N, K)) in enumerate(layers.items()):
+            n_cp = max(2, -(-ROTATE_BYTES // (4 * N * K)))
+            Ws = [make_weight(torch, N, K, 3000 + 100 * r + i, dev) for r in range(n_cp)]
             wout = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
-            fns = [(lambda e=e, n=name, o=wout: w4.fake_quant_int4_grouped(e[n][0], GF, out=o))
-                   for e in sets]
+            fns = [(lambda W=W: w4.fake_quant_int4_grouped(W, 32, out=wout)) for W in Ws]
             for f in fns:
                 f()
-            g = graph_of(torch, fns)
-            ms = time_graphs(torch, [g], max(2, reps // n_sets)) / n_sets
-            b = 4 * N * K                   # read W, write W_hat (bf16 each)
-            per[name] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1)}
+            ms = time_launches(torch, fns, max(reps, 2 * n_cp))
+            b = 4 * N * K
+            per[name] = {"us": round(ms * 1e3, 3), "GBps": round(rate(b, ms), 1)}
             tot_b += b
             tot_ms += ms
-            del g, wout, fns
+            del Ws, wout, fns
         out["fake_quant_g32"] = {
             "kernel": "quantize_kernel<32, true>", "bound": "hbm",
-            "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
-            "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes_per_set": tot_b, "set_us": round(tot_ms * 1e3, 3), "per_layer": per,
-        }
+            "achieved_GBps": round(rate(tot_b, tot_ms), 1),
+            "frac": round(rate(tot_b, tot_ms) / HBM_PEAK_GBS, 4),
+            "bytes_per_set": tot_b, "set_us": round(tot_ms * 1e3, 3), "per_layer": per}
 
-    # ---- decode GEMV on its own over rotating quantized copies ----------
-    g_ms_launch = {}
+    # ---- small-batch decode: M = 16, G = 32 and 64, outlier columns ----------
+    if want("gemv16"):
+        for Gs in (32, 64):
+            comp, _ = decode_set(
+                torch, w4, dev, layers, 16, Gs, 7000, reps, outliers=True,
+                kernel=f"gemv_split_kernel<{Gs}, 8, true, false> (qkv, o, gate_up), "
+                       f"gemv_direct_kernel<{Gs}, 8, false> (down)")
+            out[f"gemv_m16_g{Gs}"] = comp
 
-    def prep(c, s_, z, Gx, ps):
-        """Weights in the plain layout, or repacked to the pre-shuffled one."""
-        if not ps:
-            return c, s_, z
-        cp, sz = w4.repack_int4_preshuffled(c, s_, z, Gx)
-        return cp, sz, None
-
-    def lin(x, c, s_, z, Gx, y, ps):
-        if ps:
-            return lambda: w4.w4a16_linear_preshuffled(x, c, s_, Gx, out=y)
-        return lambda: w4.w4a16_linear(x, c, s_, z, Gx, out=y)
-
-    layouts = [False] if args.only in ("step", "gemv", "gemv16", "gemm") else \
-        [True] if args.only == "ps" else [False, True]
-    for ps in layouts:
-        sfx = "_ps" if ps else ""
-        if args.only not in ("all", "step", "gemv", "ps"):
-            break
-        if ps and args.only == "step":
-            break
-        gset_bytes = sum(linear_bytes(1, N, K, G) for N, K in layers.values())
-        n_g = max(2, -(-ROTATE_BYTES // gset_bytes))
-        log(f"gemv{sfx}: {n_g} rotating quantized copies of {gset_bytes / 1e6:.1f} MB")
-        gsets = []
-        for r in range(n_g):
-            src = sets[r % n_sets]
-            entry = {}
-            for name, (N, K) in layers.items():
-                W, x = src[name][0], src[name][1]
-                c, s_, z = prep(*w4.quantize_int4_grouped(W, G), G, ps)
-                entry[name] = (x, c, s_, z, torch.empty((1, N), dtype=torch.bfloat16, device=dev))
-            gsets.append(entry)
+    # ---- the 32768-square layer, G = 64: quantize pass, M = 1, M = 32768 -----
+    if want("square"):
+        NS = KS = 32768
+        Gq = 64
+        log("square 32768^2: quantize pass, M=1 linear, M=32768 linear")
+        W = make_weight(torch, NS, KS, 5, dev)
+        c, s_, z = w4.quantize_int4_grouped(W, Gq)
         torch.cuda.synchronize()
+        qfn = (lambda: w4.quantize_int4_grouped(W, Gq, c, s_, z))
+        q_ms = time_launches(torch, [qfn], 6)
+        qb = quant_bytes(NS, KS, Gq)
+        del W
+        c2, s2, z2 = w4.quantize_int4_grouped(make_weight(torch, NS, KS, 55, dev), Gq)
+        x1 = [make_x(torch, 1, KS, 5005, dev), make_x(torch, 1, KS, 5006, dev)]
+        y1 = torch.empty((1, NS), dtype=torch.bfloat16, device=dev)
+        fns = [(lambda: w4.w4a16_linear(x1[0], c, s_, z, Gq, out=y1)),
+               (lambda: w4.w4a16_linear(x1[1], c2, s2, z2, Gq, out=y1))]
+        for f in fns:
+            f()
+        m1_ms = time_launches(torch, fns, 20)
+        m1b = linear_bytes(1, NS, KS, Gq)
+        del c2, s2, z2
+        xb = make_x(torch, 32768, KS, 5007, dev)
+        yb = torch.empty((32768, NS), dtype=torch.bfloat16, device=dev)
+        big = (lambda: w4.w4a16_linear(xb, c, s_, z, Gq, out=yb))
+        big()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(2):
+            big()
+        e1.record()
+        torch.cuda.synchronize()
+        big_ms = e0.elapsed_time(e1) / 2
+        f = 2 * 32768 * NS * KS
+        out["square_32768_g64"] = {
+            "quantize": {"kernel": "quantize_kernel<64, false>", "us": round(q_ms * 1e3, 2),
+                         "bytes": qb, "GBps": round(rate(qb, q_ms), 1),
+                         "frac": round(rate(qb, q_ms) / HBM_PEAK_GBS, 4)},
+            "linear_m1": {"kernel": "gemv1_kernel<64, 8, true, false>", "us": round(m1_ms * 1e3, 2),
+                          "bytes": m1b, "GBps": round(rate(m1b, m1_ms), 1),
+                          "frac": round(rate(m1b, m1_ms) / HBM_PEAK_GBS, 4)},
+            "linear_m32768": {"kernel": "gemm_kernel<64, false>", "ms": round(big_ms, 3),
+                              "flops": f, "TFLOPs": round(f / (big_ms * 1e-3) / 1e12, 1),
+                              "frac": round(f / (big_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}}
+        del xb, yb, c, s_, z, x1, y1
 
-        def g_fn(e, name):
-            x, c, s_, z, y = e[name]
-            return lin(x, c, s_, z, G, y, ps)
+    # ---- pre-shuffled layout: decode M = 1 and prefill M = 2048 --------------
+    if want("ps"):
+        comp, _ = decode_set(torch, w4, dev, layers, 1, G, 0, reps, ps=True,
+                             kernel="gemv1_kernel<128, 4|8, false|true, true>")
+        out["gemv_m1_g128_ps"] = comp
+        out["gemm_m2048_g128_ps"] = prefill_set(torch, w4, dev, glayers, 2048, G, reps, ps=True,
+                                                kernel="gemm_kernel<128, true>")
 
-        per = {}
-        tot_ms = 0.0
-        tot_b = 0
-        for name, (N, K) in layers.items():
-            g = graph_of(torch, [g_fn(e, name) for e in gsets])
-            ms = time_graphs(torch, [g], max(2, reps // 2)) / n_g
-            if not ps:
-                g_ms_launch[name] = ms
-            b = linear_bytes(1, N, K, G)
-            per[name] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1)}
-            tot_ms += ms
-            tot_b += b
-            del g
-        # the four layers back to back, as a decode step runs them
-        g = graph_of(torch, [g_fn(e, n) for e in gsets for n in names])
-        set_ms = time_graphs(torch, [g], max(2, reps // 2)) / n_g
-        del g
-        out["gemv_m1" + sfx] = {
-            "kernel": f"gemv_split_kernel<128, 8, false, {'true' if ps else 'false'}>", "bound": "hbm",
-            "layout": "pre-shuffled" if ps else "plain",
-            "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
-            "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
-            "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes_per_set": tot_b,
-            "per_layer": per,
-            "set_back_to_back_us": round(set_ms * 1e3, 3),
-            "set_back_to_back_GBps": round(tot_b / (set_ms * 1e-3) / 1e9, 1),
-        }
-        del gsets
-
-    # ---- small-batch decode GEMV, M = 16, G = 32 (same layer shapes) ------
-    for ps in layouts:
-        sfx = "_ps" if ps else ""
-        if args.only not in ("all", "gemv16", "ps"):
-            break
-        M16, G16 = 16, 32
-        gb16 = sum(linear_bytes(M16, N, K, G16) for N, K in layers.values())
-        n16 = max(2, -(-ROTATE_BYTES // gb16))
-        log(f"gemv M=16{sfx}: {n16} rotating quantized copies of {gb16 / 1e6:.1f} MB")
-        per = {}
-        tot_ms = 0.0
-        tot_b = 0
-        for li, (name, (N, K)) in enumerate(layers.items()):
-            copies = []
-            for r in range(n16):
-                W, x = make_layer(torch, N, K, 7000 + 100 * r + li, M16, dev)
-                c, s_, z = prep(*w4.quantize_int4_grouped(W, G16), G16, ps)
-                del W
-                copies.append((x, c, s_, z, torch.empty((M16, N), dtype=torch.bfloat16, device=dev)))
-            fns = [lin(e[0], e[1], e[2], e[3], G16, e[4], ps) for e in copies]
-            g = graph_of(torch, fns)
-            ms = time_graphs(torch, [g], max(2, reps // 2)) / n16
-            b = linear_bytes(M16, N, K, G16)
-            per[name] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1)}
-            tot_ms += ms
-            tot_b += b
-            del g, copies, fns
-        t = "true" if ps else "false"
-        out["gemv_m16_g32" + sfx] = {
-            "kernel": f"gemv_split_kernel<32, 8, true, {t}> (qkv, o, gate_up), "
-                      f"gemv_direct_kernel<32, 8, {t}> (down)", "bound": "hbm",
-            "layout": "pre-shuffled" if ps else "plain",
-            "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
-            "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes_per_set": tot_b, "per_layer": per,
-        }
-
-    # ---- prefill GEMM, Gemma3-12B-shaped layers, M = 2048 ----------------
-    for ps in layouts:
-        sfx = "_ps" if ps else ""
-        if args.only not in ("all", "gemm", "ps"):
-            break
+    # ---- W4A8: per-token int8 activations + int4 weights on int8 MFMA -------
+    if want("w4a8"):
         M = 2048
-        glayers = dict(workloads.GEMMA3_12B)
-        log(f"gemm{sfx}: Gemma3-12B-shaped layers, M=2048")
-        per = {}
-        tot_ms = 0.0
-        tot_f = 0
-        for i, (name, (N, K)) in enumerate(glayers.items()):
-            W, x = make_layer(torch, N, K, 50 + i, M, dev)
-            c, s_, z = prep(*w4.quantize_int4_grouped(W, G), G, ps)
-            del W
-            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            fn = lin(x, c, s_, z, G, y, ps)
-            fn()
-            g = graph_of(torch, [fn])
-            ms = time_graphs(torch, [g], max(3, reps // 5))
-            f = 2 * M * N * K
-            per[name] = {"us": round(ms * 1e3, 2), "TFLOPs": round(f / (ms * 1e-3) / 1e12, 1)}
-            tot_ms += ms
-            tot_f += f
-            del g, x, c, s_, z, y
-        out["gemm_m2048" + sfx] = {
-            "kernel": f"gemm_kernel<128, {'true' if ps else 'false'}>", "bound": "mfma",
-            "layout": "pre-shuffled" if ps else "plain",
-            "avg_launch_us": round(tot_ms * 1e3 / len(glayers), 2),
-            "achieved_TFLOPs": round(tot_f / (tot_ms * 1e-3) / 1e12, 1),
-            "frac": round(tot_f / (tot_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "flops_per_set": tot_f,
-            "per_layer": per,
-            "set_us": round(tot_ms * 1e3, 2),
-        }
-
-    # ---- W4A8: per-token int8 activations + int4 weights on int8 MFMA -----
-    if args.only in ("all", "w4a8"):
-        M = 2048
-        glayers = dict(workloads.GEMMA3_12B)
         for Gw in (128, 32):
             log(f"w4a8 G={Gw}: Gemma3-12B-shaped layers, M=2048")
             per = {}
             tot_ms = tot_aq_ms = 0.0
             tot_f = tot_aq_b = 0
             for i, (name, (N, K)) in enumerate(glayers.items()):
-                W, x = make_layer(torch, N, K, 50 + i, M, dev)
+                W = make_weight(torch, N, K, 50 + i, dev)
                 c, s_, z = w4.quantize_int4_grouped(W, Gw)
                 del W
+                x = make_x(torch, M, K, 550 + i, dev)
                 x8, sx = w4.quantize_act_int8(x)
                 y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
                 fn = (lambda x8=x8, sx=sx, c=c, s_=s_, z=z, y=y, Gw=Gw:
                       w4.w4a8_linear(x8, sx, c, s_, z, Gw, out=y))
                 fn()
-                g = graph_of(torch, [fn])
-                ms = time_graphs(torch, [g], max(3, reps // 5))
-                del g
+                ms = time_launches(torch, [fn], max(3, reps // 5))
                 aq = (lambda x=x, x8=x8, sx=sx: w4.quantize_act_int8(x, x8=x8, sx=sx))
-                g = graph_of(torch, [aq])
-                ms_aq = time_graphs(torch, [g], max(3, reps // 5))
-                del g
+                ms_aq = time_launches(torch, [aq], max(3, reps // 5))
                 f = 2 * M * N * K
                 per[name] = {"us": round(ms * 1e3, 2), "TOPs": round(f / (ms * 1e-3) / 1e12, 1),
                              "act_quant_us": round(ms_aq * 1e3, 2)}
@@ -526,12 +673,11 @@ def main():
                 "frac": round(tot_f / (tot_ms * 1e-3) / 1e12 / MFMA_INT8_PEAK_TOPS, 4),
                 "ops_per_set": tot_f, "set_us": round(tot_ms * 1e3, 2), "per_layer": per,
                 "act_quant": {"kernel": "act_quant_kernel", "bound": "hbm",
-                              "achieved_GBps": round(tot_aq_b / (tot_aq_ms * 1e-3) / 1e9, 1),
-                              "set_us": round(tot_aq_ms * 1e3, 2)},
-            }
+                              "achieved_GBps": round(rate(tot_aq_b, tot_aq_ms), 1),
+                              "set_us": round(tot_aq_ms * 1e3, 2)}}
 
     # ---- int8 weight-only: quantizer, decode (M = 1) and prefill (M = 2048) --
-    if args.only in ("all", "w8a16"):
+    if want("w8a16"):
         def w8_bytes(M, N, K, Gq):
             return N * K + 2 * N * (K // Gq) + 2 * M * K + 2 * M * N
 
@@ -544,23 +690,18 @@ def main():
         for li, (name, (N, K)) in enumerate(layers.items()):
             copies = []
             for r in range(n8):
-                src = sets[r % n_sets][name]
-                q8, s8 = w4.quantize_int8_grouped(src[0], G)
-                copies.append((src[0], src[1], q8, s8,
+                W = make_weight(torch, N, K, 1000 * r + li, dev)
+                q8, s8 = w4.quantize_int8_grouped(W, G)
+                copies.append((W, make_x(torch, 1, K, 9000 + 1000 * r + li, dev), q8, s8,
                                torch.empty((1, N), dtype=torch.bfloat16, device=dev)))
-            g = graph_of(torch, [(lambda e=e: w4.w8a16_linear(e[1], e[2], e[3], G, out=e[4]))
-                                 for e in copies])
-            ms = time_graphs(torch, [g], max(2, reps // 2)) / n8
-            del g
-            g = graph_of(torch, [(lambda e=e: w4.quantize_int8_grouped(e[0], G, e[2], e[3]))
-                                 for e in copies])
-            ms_q = time_graphs(torch, [g], max(2, reps // 2)) / n8
-            del g
+            ms = time_launches(torch, [(lambda e=e: w4.w8a16_linear(e[1], e[2], e[3], G, out=e[4]))
+                                       for e in copies], max(reps, 2 * n8))
+            ms_q = time_launches(torch, [(lambda e=e: w4.quantize_int8_grouped(e[0], G, e[2], e[3]))
+                                         for e in copies], max(reps, 2 * n8))
             b = w8_bytes(1, N, K, G)
             bq = 3 * N * K + 2 * N * (K // G)
-            per[name] = {"us": round(ms * 1e3, 3), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
-                         "quantize_us": round(ms_q * 1e3, 3),
-                         "quantize_GBps": round(bq / (ms_q * 1e-3) / 1e9, 1)}
+            per[name] = {"us": round(ms * 1e3, 3), "GBps": round(rate(b, ms), 1),
+                         "quantize_us": round(ms_q * 1e3, 3), "quantize_GBps": round(rate(bq, ms_q), 1)}
             tot_ms += ms
             tot_b += b
             tot_q_ms += ms_q
@@ -569,32 +710,27 @@ def main():
         out["w8a16_gemv_m1"] = {
             "kernel": "w8a16_gemv_kernel<128>", "bound": "hbm",
             "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
-            "achieved_GBps": round(tot_b / (tot_ms * 1e-3) / 1e9, 1),
-            "frac": round(tot_b / (tot_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes_per_set": tot_b, "per_layer": per,
-        }
+            "achieved_GBps": round(rate(tot_b, tot_ms), 1),
+            "frac": round(rate(tot_b, tot_ms) / HBM_PEAK_GBS, 4), "bytes_per_set": tot_b,
+            "per_layer": per}
         out["quantize8_g128"] = {
             "kernel": "quantize8_kernel<128>", "bound": "hbm",
-            "achieved_GBps": round(tot_q_b / (tot_q_ms * 1e-3) / 1e9, 1),
-            "frac": round(tot_q_b / (tot_q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "bytes_per_set": tot_q_b,
-        }
+            "achieved_GBps": round(rate(tot_q_b, tot_q_ms), 1),
+            "frac": round(rate(tot_q_b, tot_q_ms) / HBM_PEAK_GBS, 4), "bytes_per_set": tot_q_b}
         M = 2048
-        glayers = dict(workloads.GEMMA3_12B)
         log("w8a16 prefill: Gemma3-12B-shaped layers, M=2048")
         per = {}
         tot_ms = 0.0
         tot_f = 0
         for i, (name, (N, K)) in enumerate(glayers.items()):
-            W, x = make_layer(torch, N, K, 50 + i, M, dev)
+            W = make_weight(torch, N, K, 50 + i, dev)
             q8, s8 = w4.quantize_int8_grouped(W, G)
             del W
+            x = make_x(torch, M, K, 550 + i, dev)
             y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             fn = (lambda x=x, q8=q8, s8=s8, y=y: w4.w8a16_linear(x, q8, s8, G, out=y))
             fn()
-            g = graph_of(torch, [fn])
-            ms = time_graphs(torch, [g], max(3, reps // 5))
-            del g
+            ms = time_launches(torch, [fn], max(3, reps // 5))
             f = 2 * M * N * K
             per[name] = {"us": round(ms * 1e3, 2), "TFLOPs": round(f / (ms * 1e-3) / 1e12, 1)}
             tot_ms += ms
@@ -604,83 +740,66 @@ def main():
             "kernel": "w8a16_gemm_kernel<128>", "bound": "mfma",
             "achieved_TFLOPs": round(tot_f / (tot_ms * 1e-3) / 1e12, 1),
             "frac": round(tot_f / (tot_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "flops_per_set": tot_f, "set_us": round(tot_ms * 1e3, 2), "per_layer": per,
-        }
+            "flops_per_set": tot_f, "set_us": round(tot_ms * 1e3, 2), "per_layer": per}
 
-    # ---- achievable-bandwidth reference: torch's own device copy ----------
-    # The same buffers calibrate the HBM byte counters: an elementwise
-    # bitwise_not is a plain kernel that reads 1 GiB and writes 1 GiB per
-    # launch (the device copy above may run as a runtime blit).
-    if args.only in ("all", "copy"):
+    # ---- torch's device copy, and the counter calibration kernel ------------
+    # An elementwise bitwise_not reads 1 GiB and writes 1 GiB per launch: the
+    # known-size kernel the HBM byte counters are scaled by.
+    if want("copy"):
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
-        g = graph_of(torch, [lambda: b.copy_(a)])
-        ms = time_graphs(torch, [g], 20)
-        del g
-        g = graph_of(torch, [lambda: torch.bitwise_not(a, out=b)])
-        ms_not = time_graphs(torch, [g], 20)
-        # read-only stream: a reduction over the same 1 GiB, timed eagerly
-        # (a multi-block reduction clears memory and stays out of graphs)
-        a32 = a.view(torch.float32)
-        for _ in range(3):
-            torch.sum(a32)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(10):
-            torch.sum(a32)
-        e1.record()
-        torch.cuda.synchronize()
-        ms_rd = e0.elapsed_time(e1) / 10
+        ms = time_launches(torch, [lambda: b.copy_(a)], 20)
+        ms_not = time_launches(torch, [lambda: torch.bitwise_not(a, out=b)], 20)
         out["hbm_reference"] = {"what": "torch device copy of 1 GiB (read + write)",
-                                "GBps": round(2 * (1 << 30) / (ms * 1e-3) / 1e9, 1),
-                                "elementwise_GBps": round(2 * (1 << 30) / (ms_not * 1e-3) / 1e9, 1),
-                                "read_only_GBps": round((1 << 30) / (ms_rd * 1e-3) / 1e9, 1)}
-        del a, b, g
+                                "GBps": round(rate(2 * (1 << 30), ms), 1),
+                                "elementwise_GBps": round(rate(2 * (1 << 30), ms_not), 1)}
+        del a, b
 
-    # ---- report ------------------------------------------------------------
-    roofline = None
-    value = None
-    if ms_per_step is not None:
-        value = step_bytes / (ms_per_step * 1e-3) / 1e9
-        # dominant kernel of the step: the one with the larger share of time
-        # (the step quantizes the four weights in one batched launch)
-        q_ms = qb_ms
-        g_ms = sum(g_ms_launch.values()) if g_ms_launch else 0.0
-        if q_ms >= g_ms:
-            b = sum(quant_bytes(N, K, G) for N, K in layers.values())
-            a_gbs = b / (q_ms * 1e-3) / 1e9
-            kname, klabel = "quantize_batch_kernel", "quantize_batch_kernel<128>"
-            nl = 1
-        else:
-            b = sum(linear_bytes(1, N, K, G) for N, K in layers.values())
-            a_gbs = b / (g_ms * 1e-3) / 1e9
-            kname, klabel = "gemv_split_kernel", "gemv_split_kernel<128, 8, false, false>"
-            nl = len(g_ms_launch)
-        tr = measured_traffic(kname)
-        roofline = {"bound": "hbm", "achieved": round(a_gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(a_gbs / HBM_PEAK_GBS, 4),
-                    "traffic": round(tr["bytes_per_launch"]) if tr else None,
-                    "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
-                                    "copy-calibrated)",
-                    "traffic_detail": tr,
-                    "kernel": klabel,
-                    "avg_launch_us": round((q_ms if q_ms >= g_ms else g_ms) * 1e3 / nl, 3),
-                    "bytes_per_launch_avg": b // nl}
-
-    for comp, kern in (("quantize", "quantize_kernel"), ("fake_quant_g32", "quantize_kernel_fake"),
-                       ("quantize_batch", "quantize_batch_kernel"),
-                       ("gemv_m1", "gemv_split_kernel"), ("gemm_m2048", "gemm_kernel"),
-                       ("gemm_m2048_ps", "gemm_kernel_ps"), ("w8a16_gemv_m1", "w8a16_gemv_kernel"),
-                       ("quantize8_g128", "quantize8_kernel"), ("w8a16_gemm_m2048", "w8a16_gemm_kernel"),
+    # ---- report --------------------------------------------------------------
+    for comp, kern in (("gemv_m1_g128", "gemv1_kernel"), ("gemm_m2048_g128", "gemm_kernel"),
+                       ("quantize_g128", "quantize_kernel"), ("fake_quant_g32", "quantize_kernel_fake"),
+                       ("quantize_batch_g128", "quantize_batch_kernel"),
+                       ("gemm_m2048_g128_ps", "gemm_kernel_ps"),
+                       ("w8a16_gemv_m1", "w8a16_gemv_kernel"), ("quantize8_g128", "quantize8_kernel"),
+                       ("w8a16_gemm_m2048", "w8a16_gemm_kernel"),
                        ("w4a8_gemm_m2048_g128", "w4a8_gemm_kernel")):
         if comp in out:
             tr = measured_traffic(kern)
             out[comp]["traffic_bytes_per_launch"] = round(tr["bytes_per_launch"]) if tr else None
 
+    value = None
+    roofline = None
+    if step is not None:
+        g = out["gemv_m1_g128"]
+        value = rate(step["bytes"], step["ms"])
+        tr = measured_traffic("gemv1_kernel")
+        roofline = {"bound": "hbm", "achieved": g["achieved_GBps"], "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": g["frac"],
+                    "traffic": round(tr["bytes_per_launch"]) if tr else None,
+                    "traffic_unit": "HBM bytes per launch, mean over the four layers "
+                                    "(rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                    "traffic_detail": tr,
+                    "kernel": g["kernel"],
+                    "avg_launch_us": g["avg_launch_us"],
+                    "bytes_per_launch_avg": g["bytes_per_set"] // len(layers),
+                    "achieved_is": "mean algorithmic bytes per launch / mean launch duration "
+                                   "(HIP events around graph replays of each layer)"}
+        if "read_stream_ceiling" in out:
+            roofline["read_stream_ceiling_GBps"] = out["read_stream_ceiling"]["decode_set_GBps"]
+    roofline_prefill = None
+    if "gemm_m2048_g128" in out:
+        g = out["gemm_m2048_g128"]
+        tr = measured_traffic("gemm_kernel")
+        roofline_prefill = {"bound": "mfma", "achieved": g["achieved_TFLOPs"],
+                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": g["frac"],
+                            "traffic": round(tr["bytes_per_launch"]) if tr else None,
+                            "kernel": g["kernel"], "avg_launch_us": g["avg_launch_us"],
+                            "workload": "gemma3_12b_prefill_layer_set_m2048_g128"}
+
     cpu = None
-    if not args.no_cpu_baseline and args.only == "all":
-        log("cpu baseline: oracle on a bounded sample")
-        cpu = cpu_baseline(layers, G)
+    if not args.no_cpu_baseline and only == "all":
+        log("cpu baseline: oracle on bounded samples")
+        cpu = cpu_baseline(G)
 
     line = {
         "metric": METRIC,
@@ -689,7 +808,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5) if ms_per_step is not None else None,
+        "ms_per_step": round(step["ms"], 6) if step is not None else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -699,14 +818,15 @@ def main():
             "workload": "llama3_8b_decode_layer_set_m1_g128",
             "layers": {k: list(v) for k, v in layers.items()},
             "M": 1, "G": G,
-            "step": "quantize the four bf16 weights (one batched launch), then "
-                    "y = x . w_hat^T per layer (M=1); one HIP graph replay per step",
-            "ms_per_step_one_quantize_launch_per_layer":
-                round(step_per_layer_ms, 5) if step_per_layer_ms is not None else None,
-            "step_bytes": step_bytes,
-            "rotating_copies": n_sets,
+            "step": "y = x . w_hat^T for the four layers back to back (M=1), one HIP graph "
+                    "replay per step, weights quantized beforehand, >= 1 GiB of weight "
+                    "copies rotated",
+            "step_bytes": step["bytes"] if step else None,
+            "rotating_copies": step["copies"] if step else None,
+            "step_wall_ms": round(step["wall_ms"], 6) if step else None,
         },
         "roofline": roofline,
+        "roofline_prefill": roofline_prefill,
         "cpu_baseline": cpu,
         "components": out,
     }

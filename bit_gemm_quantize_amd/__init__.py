@@ -15,14 +15,16 @@ import os
 from .build import LIB_PATH
 
 __all__ = [
-    "W4Status", "W4Path", "W4Error", "GROUP_SIZES", "GEMV_MAX_M", "lib",
+    "W4Status", "W4Path", "W4Error", "GROUP_SIZES", "GEMV_MAX_M", "GEMV_MAX_K", "lib",
     "repack_int4_preshuffled", "w4a16_linear_preshuffled", "quantize_act_int8", "w4a8_linear",
     "quantize_int8_grouped", "w8a16_linear", "quantize_int4_grouped_batch",
     "quantize_int4_grouped", "fake_quant_int4_grouped", "w4a16_linear", "status_string",
+    "read_stream",
 ]
 
 GROUP_SIZES = (32, 64, 128)
 GEMV_MAX_M = 16
+GEMV_MAX_K = 1 << 24  # W4_GEMV_MAX_K: AUTO sends larger K to the GEMM
 
 
 class W4Status(enum.IntEnum):
@@ -97,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.quantize_int4_grouped_batch.restype = _int
         L.w4_status_string.argtypes = [_int]
         L.w4_status_string.restype = ctypes.c_char_p
+        L.w4_read_stream.argtypes = [_p, _i64, _p, _p]
+        L.w4_read_stream.restype = _int
         _LIB = L
     return _LIB
 
@@ -392,3 +396,23 @@ def w8a16_linear(x, codes8, scales, G: int, bias=None, out=None):
     if st != W4Status.OK:
         raise W4Error(st, "w8a16_linear")
     return out
+
+
+def read_stream(buf, nbytes=None, sink=None):
+    """Read the first nbytes (default: all) of a GPU uint8 tensor once and
+    discard them (w4_read_stream): a measurement aid, the read bandwidth a
+    plain streaming kernel reaches. Returns the sink tensor."""
+    torch = _torch()
+    if not isinstance(buf, torch.Tensor) or buf.dtype != torch.uint8 or buf.device.type != "cuda":
+        raise TypeError("buf must be a uint8 GPU tensor")
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    n = buf.numel() if nbytes is None else int(nbytes)
+    if n > buf.numel():
+        raise ValueError("nbytes exceeds the buffer")
+    if sink is None:
+        sink = torch.empty(64, dtype=torch.int32, device=buf.device)
+    st = lib().w4_read_stream(buf.data_ptr(), n, sink.data_ptr(), _stream_ptr(buf.device))
+    if st != W4Status.OK:
+        raise W4Error(st, "w4_read_stream")
+    return sink

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "quantize.hip", "gemv.hip", "gemm.hip", "layout.hip", "w4a8.hip", "w8a16.hip"]
+SOURCES = ["abi.hip", "quantize.hip", "gemv.hip", "gemm.hip", "layout.hip", "w4a8.hip", "w8a16.hip",
+           "measure.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

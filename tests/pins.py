@@ -468,8 +468,31 @@ def check_int8_weights(quantize8, linear8):
     assert np.allclose(y, theirs, rtol=1e-12, atol=1e-12 * np.abs(theirs).max())
 
 
+def check_rel_frobenius(rel_frobenius):
+    """The acceptance metric ||y - y_ref||_F / ||y_ref||_F against values
+    worked out by hand, chosen so that normalising by ||y||, or taking the
+    largest element difference, gives a different number."""
+    # one difference: |(3, 0)| / |(0, 4)| = 3 / 4
+    assert rel_frobenius(np.array([3.0, 4.0]), np.array([0.0, 4.0])) == 0.75
+    # two differences (3 and 4): 5 / 4; ||y|| = sqrt(41), max |diff| = 4
+    assert rel_frobenius(np.array([3.0, 4.0, 4.0]), np.array([0.0, 4.0, 0.0])) == 1.25
+    # matrices: element-wise over all entries, 13 / 5 with diff (5, 12, 0, 0)
+    y_ref = np.array([[3.0, 0.0], [0.0, 4.0]])
+    y = y_ref + np.array([[5.0, 12.0], [0.0, 0.0]])
+    assert rel_frobenius(y, y_ref) == 13.0 / 5.0
+    # scale invariance (powers of two keep every step exact) and symmetry in sign
+    assert rel_frobenius(y * 1024.0, y_ref * 1024.0) == 13.0 / 5.0
+    assert rel_frobenius(-y, -y_ref) == 13.0 / 5.0
+    # exact agreement, and the degenerate zero reference
+    assert rel_frobenius(y_ref, y_ref) == 0.0
+    assert rel_frobenius(np.zeros(3), np.zeros(3)) == 0.0
+    assert rel_frobenius(np.ones(3), np.zeros(3)) == float("inf")
+
+
 def run_all_pins(mod):
     """Every pin against an oracle module-like object."""
+    if hasattr(mod, "rel_frobenius"):
+        check_rel_frobenius(mod.rel_frobenius)
     check_bf16_helper(mod.f32_to_bf16_bits)
     check_golden_halfsteps(mod.quantize_ref)
     check_golden_special(mod.quantize_ref)

@@ -11,6 +11,7 @@ import bit_gemm_quantize_amd as w4
 from bit_gemm_quantize_amd.build import LIB_PATH, ROOT
 
 HEADER = os.path.join(ROOT, "include", "w4a16.h")
+MEASURE_HEADER = os.path.join(ROOT, "include", "w4_measure.h")
 
 
 @pytest.fixture(scope="module")
@@ -21,8 +22,8 @@ def L():
     return w4.lib()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^[A-Za-z_][\w \t\*]*?\b(\w+)\s*\(", text, flags=re.M)
     return sorted(set(n for n in names if n not in ("defined",)))
@@ -37,9 +38,26 @@ def test_header_declares_expected_entry_points():
         "w4_status_string"])
 
 
+def test_measure_header_declares_the_stream_reference():
+    assert declared_functions(MEASURE_HEADER) == ["w4_read_stream"]
+
+
 def test_library_exports_every_declared_function(L):
-    for name in declared_functions():
+    for name in declared_functions() + declared_functions(MEASURE_HEADER):
         assert hasattr(L, name), f"{name} not exported by {LIB_PATH}"
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((None, 1024, 0x7F0000001000), w4.W4Status.ERR_NULL),
+    ((0x7F0000000000, 1024, None), w4.W4Status.ERR_NULL),
+    ((0x7F0000000000, 0, 0x7F0000001000), w4.W4Status.ERR_SHAPE),
+    ((0x7F0000000000, 1000, 0x7F0000001000), w4.W4Status.ERR_SHAPE),
+    ((0x7F0000000000, (1 << 40) + 16, 0x7F0000001000), w4.W4Status.ERR_SHAPE),
+    ((0x7F0000000008, 1024, 0x7F0000001000), w4.W4Status.ERR_ALIGN),
+    ((0x7F0000000000, 1024, 0x7F0000001004), w4.W4Status.ERR_ALIGN),
+])
+def test_read_stream_validation(L, args, expect):
+    assert L.w4_read_stream(*args, None) == expect
 
 
 def test_status_strings(L):
@@ -139,6 +157,22 @@ def lin(L, x=A, M=4, codes=B, s=C, z=D, bias=None, N=64, K=128, G=32, y=E, path=
 ])
 def test_linear_validation(L, kw, expect):
     assert lin(L, **kw) == expect
+
+
+def test_gemv_refuses_k_beyond_its_limit(L):
+    # the decode kernels address a row block with 32-bit offsets; a forced
+    # GEMV past W4_GEMV_MAX_K is refused before anything is launched
+    K = w4.GEMV_MAX_K + 128
+    for M in (1, 16):
+        assert lin(L, M=M, N=64, K=K, path=w4.W4Path.GEMV) == w4.W4Status.ERR_PATH
+        assert L.w4a16_linear_preshuffled_select(A, M, B, C, None, 64, K, 32, E,
+                                                 int(w4.W4Path.GEMV), None) == w4.W4Status.ERR_PATH
+
+
+def test_gemv_k_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+W4_GEMV_MAX_K\s+\(1 << (\d+)\)", text)
+    assert m and w4.GEMV_MAX_K == 1 << int(m.group(1))
 
 
 def test_linear_plain_entry_point_validates(L):

@@ -1,6 +1,8 @@
 """Parity at the full workload sizes, with the kernels launched as the
 benchmark launches them (automatic dispatch). Where the oracle cannot
 afford every output, it checks seeded samples of rows/columns."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -118,6 +120,29 @@ def test_square_quantize_sampled_rows(w4, square):
     for (a, b), ref in zip(square["blocks"], square["refs"]):
         got = (cd[a:b].cpu().numpy(), gu.to_host_bits(sd[a:b]), gu.to_host_bits(zd[a:b]))
         gu.assert_quant_equal(got, ref, f"square rows {a}:{b}")
+
+
+def test_square_quantize_all_rows(w4, square):
+    """The whole 32768 x 32768 quantize pass against the oracle, bit for bit,
+    in blocks of 1024 rows on the host's cores."""
+    import concurrent.futures
+    cd, sd, zd = square["dev"]
+    W, G = square["W"], square["G"]
+    got_c, got_s, got_z = cd.cpu().numpy(), gu.to_host_bits(sd), gu.to_host_bits(zd)
+    N = W.shape[0]
+    step = 1024
+
+    def block(a):
+        ref = oracle.quantize_ref(W[a:a + step], G)
+        gu.assert_quant_equal((got_c[a:a + step], got_s[a:a + step], got_z[a:a + step]), ref,
+                              f"square rows {a}:{a + step}")
+        return a
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        for i, a in enumerate(ex.map(block, range(0, N, step))):
+            if i % 8 == 7:
+                gu.log(f"square quantize: rows below {a + step} match")
 
 
 def _square_cols(square):

@@ -58,14 +58,29 @@ def test_tiny_config_auto(w4):
 GEMV_SHAPES = [(16, 128), (33, 256), (100, 96), (48, 320), (200, 1024), (17, 4096 + 128)]
 
 
-@pytest.mark.parametrize("G", [32, 64, 128])
-@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 15, 16])
-@pytest.mark.parametrize("shape", GEMV_SHAPES)
-def test_gemv(w4, G, M, shape):
-    N, K = shape
-    if K % G:
-        pytest.skip("K not a multiple of G")
+def _with_groups(cases, groups=(32, 64, 128)):
+    """(G, *case) for every group size that divides the case's K (the last
+    element of the case)."""
+    return [(G, *c) for c in cases for G in groups if c[-1] % G == 0]
+
+
+@pytest.mark.parametrize("G,M,N,K", _with_groups(
+    [(M, N, K) for M in (1, 2, 3, 5, 8, 15, 16) for N, K in GEMV_SHAPES]))
+def test_gemv(w4, G, M, N, K):
     run_case(w4, M, N, K, G, bias=(M % 2 == 1), path=gu_path(w4, "GEMV"), seed=N + K + M)
+
+
+# Edge shapes every path must take: the smallest legal K (one group of 32,
+# a single partial chunk), and fewer output rows than one 16-row tile or
+# one row group of the M = 1 kernel.
+EDGE_CASES = [(M, N, K) for M in (1, 3, 16, 17) for N, K in ((1, 32), (7, 32), (15, 64), (1, 160), (7, 4096))]
+
+
+@pytest.mark.parametrize("path,G,M,N,K", [
+    (path, *c) for c in _with_groups(EDGE_CASES) for path in ("GEMV", "GEMM")
+    if path == "GEMM" or c[1] <= 16])           # the GEMV serves M <= 16
+def test_edge_shapes(w4, path, G, M, N, K):
+    run_case(w4, M, N, K, G, bias=(N % 2 == 1), path=gu_path(w4, path), seed=11 * N + K + M)
 
 
 # Long rows: x of M rows no longer fits in LDS for the larger M, which
@@ -86,16 +101,20 @@ def test_gemv_long_k(w4, M, N, K, G):
     run_case(w4, M, N, K, G, bias=(K % 3 == 1), path=gu_path(w4, "GEMV"), seed=M + N + K)
 
 
+@pytest.mark.parametrize("K", [1 << 24, (1 << 24) + 128])
+def test_auto_dispatch_at_the_gemv_k_limit(w4, K):
+    # K = 2^24 is the largest the decode GEMV takes (its waves loop over 8192
+    # segments); one group more and AUTO hands the call to the GEMM
+    assert w4.GEMV_MAX_K == 1 << 24
+    run_case(w4, 1, 8, K, 128, bias=True, path=gu_path(w4, "AUTO"), seed=K % 1000)
+
+
 GEMM_SHAPES = [(16, 64), (130, 320), (257, 512), (64, 96)]
 
 
-@pytest.mark.parametrize("G", [32, 64, 128])
-@pytest.mark.parametrize("M", [1, 16, 17, 33, 127, 128, 129, 257])
-@pytest.mark.parametrize("shape", GEMM_SHAPES)
-def test_gemm(w4, G, M, shape):
-    N, K = shape
-    if K % G:
-        pytest.skip("K not a multiple of G")
+@pytest.mark.parametrize("G,M,N,K", _with_groups(
+    [(M, N, K) for M in (1, 16, 17, 33, 127, 128, 129, 257) for N, K in GEMM_SHAPES]))
+def test_gemm(w4, G, M, N, K):
     run_case(w4, M, N, K, G, bias=(M % 2 == 0), path=gu_path(w4, "GEMM"), seed=3 * N + K + M)
 
 

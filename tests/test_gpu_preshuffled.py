@@ -71,21 +71,29 @@ GEMV_CASES = [(1, 33, 256), (3, 100, 96 * 2), (5, 48, 320), (16, 200, 1024),
               (16, 40, 10240), (16, 40, 10016), (8, 17, 4096 + 128)]
 
 
-@pytest.mark.parametrize("G", [32, 64, 128])
-@pytest.mark.parametrize("M,N,K", GEMV_CASES)
+def _with_groups(cases, groups=(32, 64, 128)):
+    """(G, M, N, K) for every group size that divides K."""
+    return [(G, M, N, K) for M, N, K in cases for G in groups if K % G == 0]
+
+
+@pytest.mark.parametrize("G,M,N,K", _with_groups(GEMV_CASES))
 def test_gemv_preshuffled(w4, G, M, N, K):
-    if K % G:
-        pytest.skip("K not a multiple of G")
     run_case(w4, M, N, K, G, bias=(M % 2 == 1), path=w4.W4Path.GEMV, seed=N + K + M + G)
 
 
-@pytest.mark.parametrize("G", [32, 64, 128])
-@pytest.mark.parametrize("M,N,K", [(17, 64, 128), (129, 320, 256), (257, 130, 512),
-                                   (40, 96, 1024 + 32)])
+@pytest.mark.parametrize("G,M,N,K", _with_groups(
+    [(17, 64, 128), (129, 320, 256), (257, 130, 512), (40, 96, 1024 + 32)]))
 def test_gemm_preshuffled(w4, G, M, N, K):
-    if K % G:
-        pytest.skip("K not a multiple of G")
     run_case(w4, M, N, K, G, bias=(M % 2 == 0), path=w4.W4Path.GEMM, seed=3 * N + K + M)
+
+
+# smallest legal K and fewer output rows than one tile, on both paths
+@pytest.mark.parametrize("path", ["GEMV", "GEMM"])
+@pytest.mark.parametrize("G,M,N,K", _with_groups(
+    [(M, N, K) for M in (1, 3, 16) for N, K in ((1, 32), (7, 32), (15, 64), (7, 4096))]))
+def test_edge_shapes_preshuffled(w4, path, G, M, N, K):
+    run_case(w4, M, N, K, G, bias=(N % 2 == 1), path=getattr(w4.W4Path, path),
+             seed=13 * N + K + M)
 
 
 @pytest.mark.parametrize("M", [1, 16, 300])

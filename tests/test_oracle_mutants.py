@@ -77,6 +77,17 @@ MUTANTS = {
     "int8_linear_no_bias": (
         "        y = y + bf16_bits_to_f32(np.asarray(bias_bits, dtype=np.uint16)).astype(np.float64)\n    return y\n\n\ndef act_quant_ref",
         "        y = y + 0.0\n    return y\n\n\ndef act_quant_ref"),
+    "range_includes_zero": (
+        "    lo = v.min(axis=2) + np.float32(0.0)\n    hi = v.max(axis=2) + np.float32(0.0)\n",
+        "    lo = np.minimum(v.min(axis=2), np.float32(0.0)) + np.float32(0.0)\n"
+        "    hi = np.maximum(v.max(axis=2), np.float32(0.0)) + np.float32(0.0)\n"),
+    "clamp_to_14": ("np.clip(np.rint(quot), 0.0, 15.0)", "np.clip(np.rint(quot), 0.0, 14.0)"),
+    "dequant_rounded_to_bf16": (
+        "return q * np.repeat(s, G, axis=1) + np.repeat(z, G, axis=1)",
+        "return bf16_bits_to_f32(f32_to_bf16_bits((q * np.repeat(s, G, axis=1) + "
+        "np.repeat(z, G, axis=1)).astype(np.float32))).astype(np.float64)"),
+    "rel_frobenius_over_y": ("den = np.linalg.norm(y_ref)", "den = np.linalg.norm(y)"),
+    "rel_frobenius_max_abs": ("num = np.linalg.norm(y - y_ref)", "num = np.abs(y - y_ref).max()"),
     "preshuffle_sz_swapped": (
         "return codes_ps, (s | (z << np.uint32(16))).astype(np.uint32)",
         "return codes_ps, (z | (s << np.uint32(16))).astype(np.uint32)"),
