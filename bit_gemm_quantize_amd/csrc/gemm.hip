@@ -60,7 +60,38 @@ __device__ __forceinline__ void copy4(const void *g, uint32_t lds) {
                  : : "v"(g), "s"(lds) : "memory", "m0");
 }
 
-template <int G, bool PK>
+// Buffer-descriptor words for [p, p + bytes) (wave-uniform; lives in SGPRs).
+// Loads past `bytes` return 0.
+__device__ __forceinline__ u32x4 rsrc_words(const void *p, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    u32x4 r;
+    r.x = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    r.y = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    r.z = __builtin_amdgcn_readfirstlane(bytes);
+    r.w = 0x00020000u;
+    return r;
+}
+// 16 / 4 / 2 bytes per lane from buffer offset voff + soff into LDS at
+// lds (wave-uniform) + size * lane (2-byte copies: + 4 * lane, zero-extended).
+// The per-lane offset is fixed for the whole K loop and the stage advance is
+// the scalar soff, so issuing a stage costs no vector instructions.
+__device__ __forceinline__ void bcopy16(u32x4 rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 : : "v"(voff), "s"(rs), "s"(soff), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void bcopy4(u32x4 rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds"
+                 : : "v"(voff), "s"(rs), "s"(soff), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ void bcopy2(u32x4 rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_ushort %0, %1, %2 offen lds"
+                 : : "v"(voff), "s"(rs), "s"(soff), "s"(lds) : "memory", "m0");
+}
+
+// BUF: copies through buffer descriptors over the block's rows (needs
+// 128 * K * 2 < 2^32, i.e. K < 2^24); otherwise 64-bit global addresses
+// recomputed per stage.
+template <int G, bool PK, bool BUF>
 __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -108,9 +139,64 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     const int b_half = (lane & 1) ^ ((b_r >> 3) & 1);
     const uint8_t *b_src = codes + static_cast<int64_t>(min(n0 + b_r, N - 1)) * (K >> 1) + b_half * 16;
 
+    // buffer path: descriptors over the block's rows, fixed per-lane offsets
+    const int rows_m = min(BM, M - m0), rows_n = min(BN, N - n0);
+    const uint32_t kh = static_cast<uint32_t>(K) >> 1;
+    u32x4 xr = {0u, 0u, 0u, 0u}, cr = xr, sr = xr, zr = xr;
+    uint32_t xo[2] = {0u, 0u}, co = 0u, so[NSZ > 1 ? NSZ : 1] = {};
+    if constexpr (BUF) {
+        xr = rsrc_words(x + static_cast<int64_t>(m0) * K, static_cast<uint32_t>(rows_m) * K * 2);
+        cr = rsrc_words(codes + static_cast<int64_t>(n0) * kh, static_cast<uint32_t>(rows_n) * kh);
+        if constexpr (PK) {
+            sr = rsrc_words(sz + static_cast<int64_t>(n0) * ngroups, rows_n * ngroups * 4);
+        } else {
+            sr = rsrc_words(scales + static_cast<int64_t>(n0) * ngroups, rows_n * ngroups * 2);
+            zr = rsrc_words(zeros + static_cast<int64_t>(n0) * ngroups, rows_n * ngroups * 2);
+        }
+        // x copy i: row 8 (4 w + i) + lane / 8, piece (lane % 8) ^ (row / 2 % 8): the
+        // row term of copy i is 32 w + 8 i, so copies of equal i % 2 share the
+        // swizzle and differ by 8 rows
+        const uint32_t r0 = (wave * 32 + (lane >> 3)) * static_cast<uint32_t>(K);
+        xo[0] = (r0 + ((lane & 7) ^ (lane >> 4)) * 8) * 2;
+        xo[1] = (r0 + 8 * static_cast<uint32_t>(K) + ((lane & 7) ^ (4 | (lane >> 4))) * 8) * 2;
+        co = static_cast<uint32_t>(b_r) * kh + b_half * 16;
+        if constexpr (PK) {
+            so[0] = static_cast<uint32_t>((64 * wave + lane) & 127) * ngroups * 4;
+        } else {
+#pragma unroll
+            for (int d = 0; d < NSZ; ++d)
+                so[d] = static_cast<uint32_t>((64 * (NSZ * wave + d) + lane) & 127) * ngroups * 2;
+        }
+    }
+
     auto issue = [&](int kt, int buf) {
         const uint32_t base = lds0 + static_cast<uint32_t>(buf) * STAGE_BYTES;
         const int k0 = kt * KS;
+        if constexpr (BUF) {
+            const uint32_t xs = static_cast<uint32_t>(k0) * 2;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                bcopy16(xr, xo[i & 1] + (i >> 1) * 16 * static_cast<uint32_t>(K) * 2, xs,
+                        base + (wave * 4 + i) * 1024);
+            bcopy16(cr, co, static_cast<uint32_t>(k0) >> 1, base + A_BYTES + wave * 1024);
+            if constexpr (PK) {
+                const int h = (64 * wave) >> 7;
+                const int k_end = k0 + (G == 32 ? (h + 1) * 32 : KS);
+                const int g = max(0, min(k_end / G - 1, ngroups - 1));
+                bcopy4(sr, so[0], static_cast<uint32_t>(g) * 4, base + A_BYTES + B_BYTES + 256 * wave);
+            } else {
+#pragma unroll
+                for (int d = 0; d < NSZ; ++d) {
+                    const int v0 = 64 * (NSZ * wave + d);          // wave-uniform part
+                    const int isz = (v0 >> 7) & 1, h = v0 >> 8;
+                    const int k_end = k0 + (G == 32 ? (h + 1) * 32 : KS);
+                    const int g = max(0, min(k_end / G - 1, ngroups - 1));
+                    bcopy2(isz ? zr : sr, so[d], static_cast<uint32_t>(g) * 2,
+                           base + A_BYTES + B_BYTES + 64 * 4 * (NSZ * wave + d));
+                }
+            }
+            return;
+        }
         const int kp0 = min(k0 + ((lane & 7) ^ (lane >> 4)) * 8, K - 8);
         const int kp1 = min(k0 + ((lane & 7) ^ (4 | (lane >> 4))) * 8, K - 8);
 #pragma unroll
@@ -281,6 +367,7 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *codes,
                        const uint16_t *bias, int64_t N, int64_t K, int G,
                        uint16_t *y, hipStream_t stream) {
     const bool pk = sz != nullptr;
+    const bool buf = K < (int64_t(1) << 24);      // 32-bit buffer offsets over 128 rows
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     // one launch per 2^22 tiles keeps blocks x threads below 2^32
@@ -289,8 +376,15 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *codes,
         const int64_t nt = min(kMaxTiles, tiles - t0);
         const dim3 grid(static_cast<unsigned>(nt));
         const dim3 block(THREADS);
-#define W4_GEMM_LAUNCH(GG, PP) \
-    gemm_kernel<GG, PP><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt)
+#define W4_GEMM_LAUNCH(GG, PP)                                                               \
+    do {                                                                                     \
+        if (buf)                                                                             \
+            gemm_kernel<GG, PP, true><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, \
+                                                                  sz, bias, n, k, y, t0, nt); \
+        else                                                                                 \
+            gemm_kernel<GG, PP, false><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, \
+                                                                   sz, bias, n, k, y, t0, nt); \
+    } while (0)
         switch (G) {
         case 32: if (pk) W4_GEMM_LAUNCH(32, true); else W4_GEMM_LAUNCH(32, false); break;
         case 64: if (pk) W4_GEMM_LAUNCH(64, true); else W4_GEMM_LAUNCH(64, false); break;
