@@ -942,6 +942,8 @@ __global__ __launch_bounds__(GV1_MAX_WAVES * 64) void gemv1_kernel(
     const uint32_t *__restrict__ sz, const uint16_t *__restrict__ bias, int N, int K,
     uint16_t *__restrict__ y, int nseg, int nsb, int rg) {
     static_assert(R % 4 == 0, "rows per wave");
+    constexpr int GPS = GV1_SEG / G;          // groups per segment: 16, 32, 64
+    constexpr int P = R * GPS / 64;           // scale / zero-point values per lane
     // dynamic LDS: partial row sums [waves][R] f32, then (XLDS) 4 KB per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t g1_smem[];
     float *red = reinterpret_cast<float *>(g1_smem);
@@ -971,7 +973,7 @@ __global__ __launch_bounds__(GV1_MAX_WAVES * 64) void gemv1_kernel(
     for (int seg = sw; seg < nseg; seg += nsb) {
         const uint32_t k0 = static_cast<uint32_t>(seg) * GV1_SEG + 32u * lane;
         const bool ok = k0 < static_cast<uint32_t>(K);
-        // x first (needed first), then the codes, then scales / zero-points
+        // x first (needed first), then scales / zero-points, then the codes
         u32x4 xv[4];
         if constexpr (XLDS) {
 #pragma unroll
@@ -985,25 +987,33 @@ __global__ __launch_bounds__(GV1_MAX_WAVES * 64) void gemv1_kernel(
             for (int i = 0; i < 4; ++i)
                 xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, ok ? (k0 + 8 * i) * 2 : OOB, 0, 0);
         }
+        // (issued before the codes: loads complete in order, so each row can
+        // be finished as soon as its own codes arrive)
+        // Scales / zero-points of the segment's GPS groups for the R rows, P
+        // per lane: lane l holds value e = l + 64 p, i.e. row e / GPS, group
+        // e % GPS. Row r's value for this lane's group is then in register
+        // p = r GPS / 64 of lane (r GPS + group) % 64 (fetched below with a
+        // lane permute): 2P (plain) or P (pre-shuffled) loads per wave instead
+        // of 2R or R.
+        uint32_t sreg[P], zreg[P];
+#pragma unroll
+        for (int pp = 0; pp < P; ++pp) {
+            const uint32_t e = static_cast<uint32_t>(lane) + 64u * pp;
+            const uint32_t gs = static_cast<uint32_t>(seg) * GPS + e % GPS;   // group in the row
+            const uint32_t vo = (e / GPS) * ngroups + gs;
+            if constexpr (PK) {
+                sreg[pp] = __builtin_amdgcn_raw_buffer_load_b32(srs, gs < ngroups ? vo * 4 : OOB, 0, 0);
+                zreg[pp] = 0;
+            } else {
+                const uint32_t so = gs < ngroups ? vo * 2 : OOB;
+                sreg[pp] = __builtin_amdgcn_raw_buffer_load_b16(srs, so, 0, 0);
+                zreg[pp] = __builtin_amdgcn_raw_buffer_load_b16(zrs, so, 0, 0);
+            }
+        }
         u32x4 q[R];
 #pragma unroll
         for (int r = 0; r < R; ++r)
             q[r] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (k0 >> 1) + r * kh : OOB, 0, 0);
-        uint32_t sv[R], zv[R];
-        const uint32_t g = k0 / G;
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            if constexpr (PK) {
-                const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(
-                    srs, ok ? (r * ngroups + g) * 4 : OOB, 0, 0);
-                sv[r] = w & 0xFFFFu;
-                zv[r] = w >> 16;
-            } else {
-                const uint32_t so = ok ? (r * ngroups + g) * 2 : OOB;
-                sv[r] = __builtin_amdgcn_raw_buffer_load_b16(srs, so, 0, 0);
-                zv[r] = __builtin_amdgcn_raw_buffer_load_b16(zrs, so, 0, 0);
-            }
-        }
         if constexpr (XLDS) {
             // piece p -> slot 4 (p / 4) + ((p % 4) ^ ((p / 16) % 4)): the four
             // reads below (lane l: pieces 4 l .. 4 l + 3) are conflict-free
@@ -1040,8 +1050,21 @@ __global__ __launch_bounds__(GV1_MAX_WAVES * 64) void gemv1_kernel(
                 p0 = dot2_bf16(xv[i].z, w[2], p0);
                 p1 = dot2_bf16(xv[i].w, w[3], p1);
             }
-            const float s = bf16_to_f32(static_cast<uint16_t>(sv[r]));
-            const float zz = fmaf(-128.0f, s, bf16_to_f32(static_cast<uint16_t>(zv[r])));
+            // this lane's group: lane / (G / 32); source lane of row r's value
+            const int src = ((r * GPS) % 64 + lane / (G / 32)) * 4;
+            float s, z;
+            if constexpr (PK) {
+                const uint32_t w = static_cast<uint32_t>(
+                    __builtin_amdgcn_ds_bpermute(src, static_cast<int>(sreg[(r * GPS) / 64])));
+                s = bf16_lo(w);
+                z = bf16_hi(w);
+            } else {
+                s = bf16_to_f32(static_cast<uint16_t>(
+                    __builtin_amdgcn_ds_bpermute(src, static_cast<int>(sreg[(r * GPS) / 64]))));
+                z = bf16_to_f32(static_cast<uint16_t>(
+                    __builtin_amdgcn_ds_bpermute(src, static_cast<int>(zreg[(r * GPS) / 64]))));
+            }
+            const float zz = fmaf(-128.0f, s, z);
             v[r] = fmaf(s, p0 + p1, fmaf(zz, xs, v[r]));
         }
     }
@@ -1064,9 +1087,9 @@ __global__ __launch_bounds__(GV1_MAX_WAVES * 64) void gemv1_kernel(
     }
 }
 
-// M = 1: four rows per wave with x loaded directly while a row spans at
-// most two segments (K <= 4096), eight rows with x through LDS beyond
-// (measured on the Llama-3-8B decode shapes and the 32768-square layer).
+// M = 1: four rows per wave; x loaded directly while a row spans at most two
+// segments (K <= 4096), through LDS beyond (measured on the Llama-3-8B decode
+// shapes and the 32768-square layer; eight rows per wave were slower).
 template <int G, bool PK>
 hipError_t launch_gemv1(const uint16_t *x, const uint8_t *codes, const uint16_t *scales,
                         const uint16_t *zeros, const uint32_t *sz, const uint16_t *bias,
@@ -1075,19 +1098,19 @@ hipError_t launch_gemv1(const uint16_t *x, const uint8_t *codes, const uint16_t 
     const int nsb = nseg < GV1_MAX_WAVES ? nseg : GV1_MAX_WAVES;
     const int rg = nsb >= 4 ? 1 : 4 / nsb;             // about four waves per block
     const bool xlds = nseg > 2;
-    const int R = xlds ? 8 : 4;
+    constexpr int R = 4;
     const int64_t rows_per_block = static_cast<int64_t>(rg) * R;
     const unsigned blocks = static_cast<unsigned>((N + rows_per_block - 1) / rows_per_block);
     const dim3 block(static_cast<unsigned>(rg * nsb * 64));
     const size_t red_bytes = static_cast<size_t>(GV1_MAX_WAVES) * R * 4;
     if (xlds) {
-        const hipError_t e = allow_large_lds(gemv1_kernel<G, 8, true, PK>);
+        const hipError_t e = allow_large_lds(gemv1_kernel<G, R, true, PK>);
         if (e != hipSuccess) return e;
-        gemv1_kernel<G, 8, true, PK><<<dim3(blocks), block,
+        gemv1_kernel<G, R, true, PK><<<dim3(blocks), block,
                                        red_bytes + static_cast<size_t>(rg * nsb) * 4096, stream>>>(
             x, codes, scales, zeros, sz, bias, N, K, y, nseg, nsb, rg);
     } else {
-        gemv1_kernel<G, 4, false, PK><<<dim3(blocks), block, red_bytes, stream>>>(
+        gemv1_kernel<G, R, false, PK><<<dim3(blocks), block, red_bytes, stream>>>(
             x, codes, scales, zeros, sz, bias, N, K, y, nseg, nsb, rg);
     }
     return hipGetLastError();
