@@ -3,9 +3,9 @@
 Headline (``value``): the M = 1 W4A16 linear ``y = x . w_hat^T`` over the
 Llama-3-8B-shaped decode layer set (qkv, o, gate_up, down; G = 128), in GB/s
 of algorithmic HBM bytes. A step is one pass over the four layers, run back
-to back as a decode step runs them (one HIP graph replay per step), with
->= 1 GiB of distinct quantized weight copies rotated so that no cache holds
-the weights. ``roofline`` is the decode GEMV kernel against the 8 TB/s HBM
+to back as a decode step runs them (the timed steps are captured in one HIP
+graph), with >= 1 GiB of distinct quantized weight copies rotated so that no
+cache holds the weights. ``roofline`` is the decode GEMV kernel against the 8 TB/s HBM
 peak; ``roofline_prefill`` is the M = 2048 GEMM on the Gemma3-12B-shaped
 layer set against the 2.5 PFLOP/s dense bf16 matrix peak (the metric's second
 half). ``components`` times every other kernel and workload on its own (the
@@ -127,12 +127,19 @@ def graph_of(torch, fns):
     return g
 
 
-def time_graphs(torch, graphs, reps, warmup=2):
+def time_graphs(torch, graphs, reps, warmup=2, warm_ms=30.0):
     """Replay the graphs round-robin; HIP events on torch's current stream
     (the stream every launch is enqueued on) around the timed replays.
-    Returns milliseconds per replay."""
-    for i in range(warmup * len(graphs)):
+    Untimed replays first: at least ``warmup`` rounds and ``warm_ms`` of the
+    same work, so that the clocks have settled on this kernel. Returns
+    milliseconds per replay."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup * len(graphs) or (time.perf_counter() - t0) * 1e3 < warm_ms:
         graphs[i % len(graphs)].replay()
+        i += 1
+        if i % len(graphs) == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -178,46 +185,53 @@ def rate(b, ms):
 # ------------------------------------------------------------------ decode
 def decode_set(torch, w4, dev, layers, M, G, seed0, reps, ps=False, outliers=False,
                kernel="", want_step=False, steps=0, warmup=0):
-    """M-row linear on each layer over rotating quantized copies (>= 1 GiB).
-    Returns (component dict, step timing or None)."""
+    """M-row linear on each layer. Per layer: one graph of >= 64 launches over
+    >= 1 GiB of that layer's quantized copies (so no cache holds the weights
+    and graph-launch gaps are amortized). The set back to back: a graph of
+    exactly ``steps`` decode steps (the four layers, copy i % n on step i)
+    after a graph of ``warmup`` steps. Returns (component dict, step timing or
+    None)."""
     import workloads
     names = list(layers)
     set_bytes = sum(linear_bytes(M, N, K, G) for N, K in layers.values())
-    n_cp = max(2, -(-ROTATE_BYTES // set_bytes))
-    log(f"decode M={M} G={G}{' pre-shuffled' if ps else ''}: {n_cp} rotating copies "
-        f"of {set_bytes / 1e6:.1f} MB")
-    copies = []
-    for r in range(n_cp):
-        entry = {}
-        for li, (name, (N, K)) in enumerate(layers.items()):
-            oc = workloads.outlier_columns(K, seed0 + li) if outliers else None
-            W = make_weight(torch, N, K, seed0 + 1000 * r + li, dev, oc)
-            c, s_, z = w4.quantize_int4_grouped(W, G)
-            del W
-            if ps:
-                c, s_ = w4.repack_int4_preshuffled(c, s_, z, G)
-                z = None
-            x = make_x(torch, M, K, seed0 + 500 + 1000 * r + li, dev)
-            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-            entry[name] = (x, c, s_, z, y)
-        copies.append(entry)
-    torch.cuda.synchronize()
 
-    def fn(e, name):
-        x, c, s_, z, y = e[name]
+    def make_copy(name, N, K, li, r):
+        oc = workloads.outlier_columns(K, seed0 + li) if outliers else None
+        W = make_weight(torch, N, K, seed0 + 1000 * r + li, dev, oc)
+        c, s_, z = w4.quantize_int4_grouped(W, G)
+        del W
+        if ps:
+            c, s_ = w4.repack_int4_preshuffled(c, s_, z, G)
+            z = None
+        x = make_x(torch, M, K, seed0 + 500 + 1000 * r + li, dev)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        return (x, c, s_, z, y)
+
+    def fn(e):
+        x, c, s_, z, y = e
         if ps:
             return lambda: w4.w4a16_linear_preshuffled(x, c, s_, G, out=y)
         return lambda: w4.w4a16_linear(x, c, s_, z, G, out=y)
 
-    for e in copies:                        # eager warm-up of every launch
-        for name in names:
-            fn(e, name)()
     per = {}
     tot_ms = 0.0
-    for name, (N, K) in layers.items():
-        ms = time_launches(torch, [fn(e, name) for e in copies], max(reps, 2 * n_cp))
+    for li, (name, (N, K)) in enumerate(layers.items()):
         b = linear_bytes(M, N, K, G)
-        per[name] = {"us": round(ms * 1e3, 3), "GBps": round(rate(b, ms), 1), "bytes": b}
+        n_l = max(2, -(-ROTATE_BYTES // b))
+        # a few distinct weights, the rest byte copies of them (the bytes a
+        # launch reads do not change its time; only that they are not cached)
+        base = [make_copy(name, N, K, li, r) for r in range(min(n_l, 4))]
+        cps = [tuple(t.clone() if t is not None else None for t in base[r % len(base)])
+               for r in range(n_l)]
+        del base
+        for e in cps:
+            fn(e)()
+        fns = [fn(e) for e in cps] * max(1, -(-64 // n_l))
+        g = graph_of(torch, fns)
+        ms = time_graphs(torch, [g], max(2, -(-reps // len(fns)))) / len(fns)
+        del g, fns, cps
+        per[name] = {"us": round(ms * 1e3, 3), "GBps": round(rate(b, ms), 1), "bytes": b,
+                     "rotating_copies": n_l}
         tot_ms += ms
     comp = {
         "kernel": kernel, "bound": "hbm", "M": M, "G": G,
@@ -225,34 +239,60 @@ def decode_set(torch, w4, dev, layers, M, G, seed0, reps, ps=False, outliers=Fal
         "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
         "achieved_GBps": round(rate(set_bytes, tot_ms), 1),
         "frac": round(rate(set_bytes, tot_ms) / HBM_PEAK_GBS, 4),
-        "bytes_per_set": set_bytes, "per_layer": per, "rotating_copies": n_cp,
+        "bytes_per_set": set_bytes, "per_layer": per,
     }
+    # the four layers back to back, as a decode step runs them
+    n_cp = max(2, -(-ROTATE_BYTES // set_bytes))
+    log(f"decode M={M} G={G}{' pre-shuffled' if ps else ''}: set back to back over "
+        f"{n_cp} rotating copies of {set_bytes / 1e6:.1f} MB")
+    copies = [{name: make_copy(name, N, K, li, r) for li, (name, (N, K)) in enumerate(layers.items())}
+              for r in range(n_cp)]
+    torch.cuda.synchronize()
+
+    def step_fns(n):
+        return [fn(copies[i % n_cp][name]) for i in range(n) for name in names]
+
+    for f in step_fns(n_cp):
+        f()
+    comp["rotating_copies"] = n_cp
     step = None
-    # the four layers back to back, one graph per copy, as a decode step runs them
-    graphs = [graph_of(torch, [fn(e, n) for n in names]) for e in copies]
+    n_timed = max(steps, 1) if want_step else max(2 * n_cp, reps)
+    g_warm = graph_of(torch, step_fns(max(warmup, 1)))
+    g_time = graph_of(torch, step_fns(n_timed))
     if want_step:
-        log(f"decode step: warmup {warmup}, timed {steps} (graph replays)")
-        for i in range(warmup):
-            graphs[i % n_cp].replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record()
-        for i in range(steps):
-            graphs[i % n_cp].replay()
-        e1.record()
-        torch.cuda.synchronize()
-        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-        step = {"ms": e0.elapsed_time(e1) / steps, "wall_ms": wall_ms, "bytes": set_bytes,
-                "copies": n_cp}
-        comp["set_back_to_back_us"] = round(step["ms"] * 1e3, 3)
-    else:
-        set_ms = time_graphs(torch, graphs, max(2 * n_cp, reps // 2))
-        comp["set_back_to_back_us"] = round(set_ms * 1e3, 3)
-    comp["set_back_to_back_GBps"] = round(rate(set_bytes, comp["set_back_to_back_us"] * 1e-3), 1)
-    del graphs, copies
+        log(f"decode step: warmup {warmup}, timed {n_timed} (one graph of {n_timed} steps)")
+    g_warm.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    g_time.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / n_timed
+    set_ms = e0.elapsed_time(e1) / n_timed
+    if want_step:
+        step = {"ms": set_ms, "wall_ms": wall_ms, "bytes": set_bytes, "copies": n_cp}
+    comp["set_back_to_back_us"] = round(set_ms * 1e3, 3)
+    comp["set_back_to_back_GBps"] = round(rate(set_bytes, set_ms), 1)
+    del g_warm, g_time, copies
     return comp, step
+
+
+def warm_gpu(torch, w4, dev, seconds=1.0):
+    """Sustained streaming reads for about ``seconds`` before anything is
+    timed, so that the first measurement does not pay for the clocks and
+    memory system coming out of idle."""
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    buf.fill_(0x5A)
+    sink = torch.empty(64, dtype=torch.int32, device=dev)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            w4.read_stream(buf, buf.numel(), sink)
+        torch.cuda.synchronize()
+    del buf
 
 
 def stream_ceiling(torch, w4, dev, sizes, reps):
@@ -459,13 +499,16 @@ def main():
     def want(*parts):
         return only == "all" or only in parts
 
+    if only != "copy":
+        warm_gpu(torch, w4, dev)
+
     # ---- headline: M = 1 linear over the decode set --------------------------
     step = None
     if want("decode"):
         comp, step = decode_set(
             torch, w4, dev, layers, 1, G, 0, reps,
             kernel="gemv1_kernel<128, 4, false, false> (qkv, o, gate_up), "
-                   "gemv1_kernel<128, 8, true, false> (down)",
+                   "gemv1_kernel<128, 4, true, false> (down)",
             want_step=True, steps=max(args.steps, 1), warmup=args.warmup)
         out["gemv_m1_g128"] = comp
     if want("decode", "stream"):
@@ -527,7 +570,7 @@ def main():
                 "ms": round(ms, 5), "bytes": sb, "GBps": round(rate(sb, ms), 1)}
         qb_ms = time_launches(torch, [qbatch(e) for e in sets], max(reps, 2 * n_sets))
         out["quantize_batch_g128"] = {
-            "kernel": "quantize_batch_kernel<128>", "bound": "hbm",
+            "kernel": "quantize_batch_kernel<128, 2>", "bound": "hbm",
             "avg_launch_us": round(qb_ms * 1e3, 3), "bytes_per_launch": set_qbytes,
             "achieved_GBps": round(rate(set_qbytes, qb_ms), 1),
             "frac": round(rate(set_qbytes, qb_ms) / HBM_PEAK_GBS, 4)}
@@ -543,7 +586,7 @@ def main():
             tot_b += b
             tot_ms += ms
         out["quantize_g128"] = {
-            "kernel": "quantize_kernel<128, false>", "bound": "hbm",
+            "kernel": "quantize_kernel<128, false, 2>", "bound": "hbm",
             "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
             "achieved_GBps": round(rate(tot_b, tot_ms), 1),
             "frac": round(rate(tot_b, tot_ms) / HBM_PEAK_GBS, 4),
@@ -569,7 +612,7 @@ def main():
             tot_ms += ms
             del Ws, wout, fns
         out["fake_quant_g32"] = {
-            "kernel": "quantize_kernel<32, true>", "bound": "hbm",
+            "kernel": "quantize_kernel<32, true, 2>", "bound": "hbm",
             "achieved_GBps": round(rate(tot_b, tot_ms), 1),
             "frac": round(rate(tot_b, tot_ms) / HBM_PEAK_GBS, 4),
             "bytes_per_set": tot_b, "set_us": round(tot_ms * 1e3, 3), "per_layer": per}
@@ -619,10 +662,10 @@ def main():
         big_ms = e0.elapsed_time(e1) / 2
         f = 2 * 32768 * NS * KS
         out["square_32768_g64"] = {
-            "quantize": {"kernel": "quantize_kernel<64, false>", "us": round(q_ms * 1e3, 2),
+            "quantize": {"kernel": "quantize_kernel<64, false, 2>", "us": round(q_ms * 1e3, 2),
                          "bytes": qb, "GBps": round(rate(qb, q_ms), 1),
                          "frac": round(rate(qb, q_ms) / HBM_PEAK_GBS, 4)},
-            "linear_m1": {"kernel": "gemv1_kernel<64, 8, true, false>", "us": round(m1_ms * 1e3, 2),
+            "linear_m1": {"kernel": "gemv1_kernel<64, 4, true, false>", "us": round(m1_ms * 1e3, 2),
                           "bytes": m1b, "GBps": round(rate(m1b, m1_ms), 1),
                           "frac": round(rate(m1b, m1_ms) / HBM_PEAK_GBS, 4)},
             "linear_m32768": {"kernel": "gemm_kernel<64, false>", "ms": round(big_ms, 3),
@@ -633,7 +676,7 @@ def main():
     # ---- pre-shuffled layout: decode M = 1 and prefill M = 2048 --------------
     if want("ps"):
         comp, _ = decode_set(torch, w4, dev, layers, 1, G, 0, reps, ps=True,
-                             kernel="gemv1_kernel<128, 4|8, false|true, true>")
+                             kernel="gemv1_kernel<128, 4, false|true, true>")
         out["gemv_m1_g128_ps"] = comp
         out["gemm_m2048_g128_ps"] = prefill_set(torch, w4, dev, glayers, 2048, G, reps, ps=True,
                                                 kernel="gemm_kernel<128, true>")
@@ -783,7 +826,8 @@ def main():
                     "avg_launch_us": g["avg_launch_us"],
                     "bytes_per_launch_avg": g["bytes_per_set"] // len(layers),
                     "achieved_is": "mean algorithmic bytes per launch / mean launch duration "
-                                   "(HIP events around graph replays of each layer)"}
+                                   "(HIP events around a graph of >= 64 launches of each "
+                                   "layer over >= 1 GiB of its copies)"}
         if "read_stream_ceiling" in out:
             roofline["read_stream_ceiling_GBps"] = out["read_stream_ceiling"]["decode_set_GBps"]
     roofline_prefill = None
@@ -818,9 +862,9 @@ def main():
             "workload": "llama3_8b_decode_layer_set_m1_g128",
             "layers": {k: list(v) for k, v in layers.items()},
             "M": 1, "G": G,
-            "step": "y = x . w_hat^T for the four layers back to back (M=1), one HIP graph "
-                    "replay per step, weights quantized beforehand, >= 1 GiB of weight "
-                    "copies rotated",
+            "step": "y = x . w_hat^T for the four layers back to back (M=1); the K timed "
+                    "steps are one HIP graph of 4K launches, weights quantized beforehand, "
+                    ">= 1 GiB of weight copies rotated",
             "step_bytes": step["bytes"] if step else None,
             "rotating_copies": step["copies"] if step else None,
             "step_wall_ms": round(step["wall_ms"], 6) if step else None,

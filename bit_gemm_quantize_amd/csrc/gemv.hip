@@ -161,7 +161,7 @@ __device__ __forceinline__ void load_batch_buf(Batch<G, U> &b, __amdgpu_buffer_r
     for (int u = 0; u < U; ++u) {
         // chunks past this wave's segment are never computed: not fetched
         const int so = c + u <= c_last ? (c + u) * 64 : OOB;
-        b.q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo, so, 0);
+        b.q[u] = __builtin_amdgcn_raw_buffer_load_b128(crs, cvo, so, W4_CPOL_STREAM);
     }
 }
 
@@ -1013,7 +1013,8 @@ __global__ __launch_bounds__(GV1_MAX_WAVES * 64) void gemv1_kernel(
         u32x4 q[R];
 #pragma unroll
         for (int r = 0; r < R; ++r)
-            q[r] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (k0 >> 1) + r * kh : OOB, 0, 0);
+            q[r] = __builtin_amdgcn_raw_buffer_load_b128(crs, ok ? (k0 >> 1) + r * kh : OOB, 0,
+                                                         W4_CPOL_STREAM);
         if constexpr (XLDS) {
             // piece p -> slot 4 (p / 4) + ((p % 4) ^ ((p / 16) % 4)): the four
             // reads below (lane l: pieces 4 l .. 4 l + 3) are conflict-free

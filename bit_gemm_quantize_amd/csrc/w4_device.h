@@ -161,6 +161,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, bytes, 0x00020000);
 }
 
+// Cache-policy operand for weights a kernel reads exactly once (the GEMVs):
+// nt, streaming, so the lines are not kept in L2 and the reused operands (x,
+// scales) stay there.
+constexpr int W4_CPOL_STREAM = 2;
+
 // bf16 1.0 in every element.
 __device__ __forceinline__ bf16x8 bf16x8_ones() {
     return as_bf16x8(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);

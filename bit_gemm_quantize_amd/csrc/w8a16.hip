@@ -360,7 +360,7 @@ __global__ __launch_bounds__(GV8_WAVES * 64, 2) void w8a16_gemv_kernel(
         const int xs = live ? j * 128 : OOB;
         xa[slot][0] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 2 * xk0, xs, 0);
         xa[slot][1] = __builtin_amdgcn_raw_buffer_load_b128(xrs, xo + 2 * xk1, xs, 0);
-        wb[slot] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wo, live ? j * 64 : OOB, 0);
+        wb[slot] = __builtin_amdgcn_raw_buffer_load_b128(wrs, wo, live ? j * 64 : OOB, W4_CPOL_STREAM);
         // the scale rides with the slice that folds its group; the 16 lanes
         // of the first row load it (the fold broadcasts it to the others)
         if constexpr (PAIR) {
