@@ -45,7 +45,8 @@ KERNEL_SOURCES = {
     "quantize_kernel_fake": ["quantize.hip", "w4_device.h"],
     "quantize_batch_kernel": ["quantize.hip", "w4_device.h"],
     "gemv1_kernel": ["gemv.hip", "w4_device.h"],
-    "gemv_split_kernel": ["gemv.hip", "w4_device.h"],
+    "gemv_split_kernel_g32": ["gemv.hip", "w4_device.h"],
+    "gemv_split_kernel_g64": ["gemv.hip", "w4_device.h"],
     "gemm_kernel": ["gemm.hip", "w4_device.h"],
     "gemm_kernel_ps": ["gemm.hip", "w4_device.h"],
     "quantize8_kernel": ["w8a16.hip", "w4_device.h"],
@@ -805,7 +806,9 @@ def main():
                        ("gemm_m2048_g128_ps", "gemm_kernel_ps"),
                        ("w8a16_gemv_m1", "w8a16_gemv_kernel"), ("quantize8_g128", "quantize8_kernel"),
                        ("w8a16_gemm_m2048", "w8a16_gemm_kernel"),
-                       ("w4a8_gemm_m2048_g128", "w4a8_gemm_kernel")):
+                       ("w4a8_gemm_m2048_g128", "w4a8_gemm_kernel"),
+                       ("gemv_m16_g32", "gemv_split_kernel_g32"),
+                       ("gemv_m16_g64", "gemv_split_kernel_g64")):
         if comp in out:
             tr = measured_traffic(kern)
             out[comp]["traffic_bytes_per_launch"] = round(tr["bytes_per_launch"]) if tr else None
