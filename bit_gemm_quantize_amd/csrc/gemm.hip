@@ -232,6 +232,19 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
         }
     };
 
+    // Per-lane byte offsets of the fragments inside a stage buffer, slice 0
+    // and 1. x row r = 64 wm + 16 mt + nl holds k-piece p in slot
+    // p ^ ((r / 2) % 8) (= p ^ ((nl / 2) % 8): the tile steps keep it); code
+    // row r = 64 wn + 16 nt + nl holds its k-half h in half h ^ ((r / 8) % 2)
+    // (= h ^ ((nl / 8) % 2)). Kept opaque so that they stay in registers
+    // instead of being recomputed in every slice.
+    uint32_t la[2], lb[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        la[s] = static_cast<uint32_t>((wm * 64 + nl) * 128 + (((s * 4 + kb) ^ ((nl >> 1) & 7)) * 16));
+        lb[s] = static_cast<uint32_t>(A_BYTES + (wn * 64 + nl) * 32 + ((s ^ ((nl >> 3) & 1)) * 16) + kb * 4);
+        asm volatile("" : "+v"(la[s]), "+v"(lb[s]));
+    }
     f32x4 acc[4][4], accg[4][4], xsg[4];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -257,18 +270,17 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
         constexpr bool first = G == 128 ? (par == 0 && sl == 0) : (G == 64 ? sl == 0 : true);
         constexpr bool last = G == 128 ? (par == 1 && sl == 1) : (G == 64 ? sl == 1 : true);
         const uint8_t *sb = &smem[buf][0];
+        // one add per operand and slice: the per-lane offsets are fixed, the
+        // m- / n-tile steps are immediates
+        const uint8_t *sa = sb + la[sl];
+        const uint8_t *sw = sb + lb[sl];
         bf16x8 a[4], b[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const int r = wm * 64 + mt * 16 + nl;
-            a[mt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(
-                sb + r * 128 + (((sl * 4 + kb) ^ ((r >> 1) & 7)) * 16)));
-        }
+        for (int mt = 0; mt < 4; ++mt)
+            a[mt] = as_bf16x8(*reinterpret_cast<const u32x4 *>(sa + mt * 16 * 128));
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-            const int r = wn * 64 + nt * 16 + nl;
-            const uint32_t w = *reinterpret_cast<const uint32_t *>(
-                sb + A_BYTES + r * 32 + ((sl ^ ((r >> 3) & 1)) * 16) + kb * 4);
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(sw + nt * 16 * 32);
             uint32_t u[4];
             if constexpr (PK)
                 unpack8_bias128_il(w, u, uc);    // pre-shuffled: natural k order
@@ -314,7 +326,11 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     __syncthreads();
 
     auto stage = [&](auto par_c, int kt) {
-        const int buf = kt % NBUF;
+        // the buffer index is made opaque: left visible, the compiler turns
+        // it into a per-lane induction variable that costs two vector ops
+        // per fragment read (a scalar offset costs one)
+        int buf = kt % NBUF;
+        asm volatile("" : "+s"(buf));
         // stage kt + 2 goes into the buffer read in stage kt - 1 (every wave
         // is past the barrier that ended it); past the end it repeats the
         // last stage into a buffer that is not read again
