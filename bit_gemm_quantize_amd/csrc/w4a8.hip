@@ -304,7 +304,10 @@ __global__ __launch_bounds__(THREADS, 2) void w4a8_gemm_kernel(
     __syncthreads();
 
     auto step = [&](auto par_c, int kt) {
-        const int buf = kt % NBUF;
+        // opaque buffer index: a scalar offset per fragment read instead of a
+        // per-lane induction variable
+        int buf = kt % NBUF;
+        asm volatile("" : "+s"(buf));
         // stage kt + 2 goes into the buffer read in stage kt - 1; past the
         // end it repeats the last stage into a buffer that is not read again
         issue(min(kt + 2, nstages - 1), (kt + 2) % NBUF);

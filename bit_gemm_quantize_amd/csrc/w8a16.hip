@@ -256,7 +256,10 @@ __global__ __launch_bounds__(THREADS, 2) void w8a16_gemm_kernel(
     __syncthreads();
 
     auto stage = [&](auto par_c, int kt) {
-        const int buf = kt % NBUF;
+        // opaque buffer index: a scalar offset per fragment read instead of a
+        // per-lane induction variable
+        int buf = kt % NBUF;
+        asm volatile("" : "+s"(buf));
         issue(min(kt + 2, nstages - 1), (kt + 2) % NBUF);
         slice(buf, par_c, IC<0>{});
         slice(buf, par_c, IC<1>{});
