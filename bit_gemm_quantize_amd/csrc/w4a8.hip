@@ -88,6 +88,86 @@ __global__ __launch_bounds__(AQ_THREADS) void act_quant_kernel(const uint16_t *_
     }
 }
 
+// Rows of up to 256 PPT 16-byte pieces (K <= 2048 PPT): each thread keeps
+// its pieces in registers between the max pass and the codes (one read of
+// the row), and divides by a reciprocal multiply checked against the exact
+// quotient's rounding. With s in [2^-100, 2^100] the hardware reciprocal is
+// within 1 ulp, so t = x * rcp(s) is within |t| 1.5 2^-23 <= 2^-15 of x / s,
+// and the binary32 quotient within half an ulp of it (< 2^-17 at |t| <=
+// 127); when every t of a piece is farther than 2^-14 from a half-integer,
+// rint(t) equals rint of the binary32 quotient, otherwise (or for extreme
+// scales) the piece is redone with the true divide.
+template <int PPT>
+__global__ __launch_bounds__(AQ_THREADS) void act_quant_reg_kernel(const uint16_t *__restrict__ x,
+                                                                    int K, int8_t *__restrict__ x8,
+                                                                    float *__restrict__ sx) {
+    __shared__ float wmax[AQ_THREADS / 64];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int n8 = K >> 3;                       // 16-byte pieces (K % 32 == 0)
+    const __amdgpu_buffer_rsrc_t xr = buf_rsrc(x + row * K, static_cast<uint32_t>(K) * 2);
+    const __amdgpu_buffer_rsrc_t qr = buf_rsrc(x8 + row * K, static_cast<uint32_t>(K));
+    u32x4 v[PPT];
+#pragma unroll
+    for (int i = 0; i < PPT; ++i)                // pieces past the row read 0
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(xr, (tid + AQ_THREADS * i) * 16, 0,
+                                                     W4_CPOL_STREAM);
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        a = fmaxf(a, fmaxf(fmaxf(fabsf(bf16_lo(v[i].x)), fabsf(bf16_hi(v[i].x))),
+                           fmaxf(fabsf(bf16_lo(v[i].y)), fabsf(bf16_hi(v[i].y)))));
+        a = fmaxf(a, fmaxf(fmaxf(fabsf(bf16_lo(v[i].z)), fabsf(bf16_hi(v[i].z))),
+                           fmaxf(fabsf(bf16_lo(v[i].w)), fabsf(bf16_hi(v[i].w)))));
+    }
+    a = fmaxf(a, dpp_f32<DPP_QUAD_XOR1>(a));
+    a = fmaxf(a, dpp_f32<DPP_QUAD_XOR2>(a));
+    a = fmaxf(a, dpp_f32<DPP_ROW_HALF_MIRROR>(a));
+    a = fmaxf(a, dpp_f32<DPP_ROW_MIRROR>(a));
+    a = fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 0)),
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 16))),
+              fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 32)),
+                    __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 48))));
+    if ((tid & 63) == 0) wmax[tid >> 6] = a;
+    __syncthreads();
+    float amax = wmax[0];
+#pragma unroll
+    for (int w = 1; w < AQ_THREADS / 64; ++w) amax = fmaxf(amax, wmax[w]);
+    const float s = amax / 127.0f;               // correctly rounded (build flag)
+    if (tid == 0) sx[row] = s;
+    const bool fast = s >= 0x1p-100f && s <= 0x1p100f;
+    const float r = __builtin_amdgcn_rcpf(s);
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+        const int p = tid + AQ_THREADS * i;
+        if (p >= n8) break;                      // only the last piece can lie past the row
+        const float f[8] = {bf16_lo(v[i].x), bf16_hi(v[i].x), bf16_lo(v[i].y), bf16_hi(v[i].y),
+                            bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
+        float q[8];
+        float dmax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float t = f[e] * r;
+            q[e] = __builtin_rintf(t);
+            dmax = fmaxf(dmax, fabsf(t - q[e]));
+        }
+        if (s == 0.0f) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q[e] = 0.0f;
+        } else if (!fast || !(dmax < 0.5f - 0x1p-14f)) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) q[e] = __builtin_rintf(f[e] / s);
+        }
+        uint32_t o[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float c = fminf(fmaxf(q[e], -127.0f), 127.0f);
+            o[e >> 2] |= (static_cast<uint32_t>(static_cast<int>(c)) & 0xFFu) << (8 * (e & 3));
+        }
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{o[0], o[1]}, qr, p * 8, 0, W4_CPOL_STREAM);
+    }
+}
+
 // ---------------------------------------------------------------- GEMM
 constexpr int BM = 128, BN = 128, KS = 64;
 constexpr int THREADS = 256;
@@ -354,10 +434,24 @@ __global__ __launch_bounds__(THREADS, 2) void w4a8_gemm_kernel(
 hipError_t launch_act_quant(const uint16_t *x, int64_t M, int64_t K, int8_t *x8, float *sx,
                             hipStream_t stream) {
     constexpr int64_t kMaxRows = int64_t(1) << 30;
+    // pieces of 8 per thread when the row fits in registers (K <= 16384)
+    const int64_t ppt = (K / 8 + AQ_THREADS - 1) / AQ_THREADS;
     for (int64_t r0 = 0; r0 < M; r0 += kMaxRows) {
         const int64_t rows = M - r0 < kMaxRows ? M - r0 : kMaxRows;
-        act_quant_kernel<<<dim3(static_cast<unsigned>(rows)), dim3(AQ_THREADS), 0, stream>>>(
-            x + r0 * K, static_cast<int>(K), x8 + r0 * K, sx + r0);
+        const dim3 grid(static_cast<unsigned>(rows)), block(AQ_THREADS);
+        const int k = static_cast<int>(K);
+        switch (ppt) {
+        case 1: act_quant_reg_kernel<1><<<grid, block, 0, stream>>>(x + r0 * K, k, x8 + r0 * K, sx + r0); break;
+        case 2: act_quant_reg_kernel<2><<<grid, block, 0, stream>>>(x + r0 * K, k, x8 + r0 * K, sx + r0); break;
+        case 3: act_quant_reg_kernel<3><<<grid, block, 0, stream>>>(x + r0 * K, k, x8 + r0 * K, sx + r0); break;
+        case 4: act_quant_reg_kernel<4><<<grid, block, 0, stream>>>(x + r0 * K, k, x8 + r0 * K, sx + r0); break;
+        case 5: case 6:
+            act_quant_reg_kernel<6><<<grid, block, 0, stream>>>(x + r0 * K, k, x8 + r0 * K, sx + r0); break;
+        case 7: case 8:
+            act_quant_reg_kernel<8><<<grid, block, 0, stream>>>(x + r0 * K, k, x8 + r0 * K, sx + r0); break;
+        default:
+            act_quant_kernel<<<grid, block, 0, stream>>>(x + r0 * K, k, x8 + r0 * K, sx + r0);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

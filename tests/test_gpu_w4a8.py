@@ -9,6 +9,7 @@ import torch
 import oracle
 import workloads
 from tests import gpu_util as gu
+from tests import pins
 
 pytestmark = pytest.mark.gpu
 
@@ -46,6 +47,31 @@ def test_act_quant_bit_exact(w4, M, K):
     if M > 2:
         x[2, 5] = workloads.random_bf16((1, 1), 50.0, 3)[0, 0]   # an outlier
     act_checked(w4, x, f"M={M} K={K}")
+
+
+@pytest.mark.parametrize("K", [64, 2048, 3840, 8192, 8192 + 32, 15360, 16384 + 32])
+def test_act_quant_rounding_edges(w4, K):
+    """Rows whose quotients land on or next to half-integers (scale 1 with
+    exact ties; half the row maximum within an ulp of 63.5, where a
+    reciprocal multiply and the binary32 quotient round apart; a quarter
+    grid), rows spanning eight decades, subnormal and huge scales, and a zero
+    row, at row lengths held in registers (K <= 16384) and beyond."""
+    rng = np.random.default_rng(K)
+    V = rng.uniform(-1.0, 1.0, (10, K))
+    V[0, :10] = [1.0, -0.5, 0.25, -0.75, 0.0, -0.0, 127.0, 63.5, 2.5, -3.5]   # scale 1
+    V[0, 10:] = np.round(V[0, 10:] * 254.0) / 2.0                               # more ties
+    V[1, :2] = [43.75, 21.875]
+    V[2, :2] = [-89.5, 44.75]
+    V[3] = np.round(rng.uniform(-50.0, 50.0, K) * 4.0) / 4.0
+    V[4] = rng.standard_normal(K) * 10.0 ** rng.integers(-4, 4, K)
+    V[5] = rng.uniform(-1.0, 1.0, K) * 1e-38        # scale far below 2^-100
+    V[6] = rng.uniform(-1.0, 1.0, K) * 1e38         # scale above 2^100
+    V[7] = 0.0
+    # a row maximum of 127 * 2^j: scale 2^j, every x / s exact
+    V[8] = np.round(rng.uniform(-127.0, 127.0, K) * 2.0) / 2.0 * 2.0 ** -20
+    V[8, 0] = 127.0 * 2.0 ** -20
+    V[9] = -V[1]
+    act_checked(w4, pins.bf16_from_float(V), f"rounding edges K={K}")
 
 
 def run_case(w4, M, N, K, G, bias, seed, outliers=False):
