@@ -128,12 +128,13 @@ def graph_of(torch, fns):
     return g
 
 
-def time_graphs(torch, graphs, reps, warmup=2, warm_ms=30.0):
+def time_graphs(torch, graphs, reps, warmup=2, warm_ms=30.0, passes=3):
     """Replay the graphs round-robin; HIP events on torch's current stream
     (the stream every launch is enqueued on) around the timed replays.
     Untimed replays first: at least ``warmup`` rounds and ``warm_ms`` of the
-    same work, so that the clocks have settled on this kernel. Returns
-    milliseconds per replay."""
+    same work, so that the clocks have settled on this kernel. Then
+    ``passes`` timed passes of ``reps`` replays each. Returns milliseconds
+    per replay: the median over the passes of each pass's mean."""
     t0 = time.perf_counter()
     i = 0
     while i < warmup * len(graphs) or (time.perf_counter() - t0) * 1e3 < warm_ms:
@@ -142,14 +143,17 @@ def time_graphs(torch, graphs, reps, warmup=2, warm_ms=30.0):
         if i % len(graphs) == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(reps):
-        graphs[i % len(graphs)].replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    per = []
+    for _ in range(max(1, passes)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            graphs[i % len(graphs)].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) / reps)
+    return sorted(per)[len(per) // 2]
 
 
 def time_launches(torch, fns, reps):
