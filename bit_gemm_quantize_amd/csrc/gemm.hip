@@ -4,7 +4,8 @@
 //   sum_g ( s[n][g] * sum_{k in g} x[m][k] q[n][k] + z[n][g] * sum_{k in g} x[m][k] )
 // ("Optimum Quanto": wide accumulation, then dequantization; bias in float).
 //
-// Block tile 128 (m) x 128 (n), four waves in a 2 x 2 grid, 64 x 64 each.
+// Block tile 128 (m) x BN (n), BN = 128 (four waves in a 2 x 2 grid) or 256
+// (eight waves in a 2 x 4 grid), 64 x 64 per wave.
 // K advances in stages of 64 (two 32-wide slices) through three LDS buffers,
 // two stages in flight while one is computed. Every operand reaches LDS by a
 // direct global -> LDS copy issued from asm (16 bytes per lane; scales and
@@ -33,13 +34,9 @@ namespace w4 {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, KS = 64;
-constexpr int THREADS = 256;
+constexpr int BM = 128, KS = 64;
 constexpr int NBUF = 3;                          // stages in LDS (two in flight)
 constexpr int A_BYTES = BM * KS * 2;             // x tile, bf16, swizzled rows
-constexpr int B_BYTES = BN * KS / 2;             // code tile, packed nibbles
-constexpr int SZ_BYTES = 2 * 2 * BN * 4;         // [group end][s | z][row], 4 B each
-constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SZ_BYTES;
 
 template <int V>
 using IC = std::integral_constant<int, V>;
@@ -90,23 +87,33 @@ __device__ __forceinline__ void bcopy2(u32x4 rs, uint32_t voff, uint32_t soff, u
 
 // BUF: copies through buffer descriptors over the block's rows (needs
 // 128 * K * 2 < 2^32, i.e. K < 2^24); otherwise 64-bit global addresses
-// recomputed per stage.
-template <int G, bool PK, bool BUF>
-__global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
+// recomputed per stage. BNT: block tile columns, 128 or 256 (2 BNT threads;
+// per stage the x tile is shared by BNT / 64 wave columns, so the wider
+// block issues a third fewer copies per MFMA).
+template <int G, bool PK, bool BUF, int BNT>
+__global__ __launch_bounds__(BNT * 2, 2) void gemm_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     const uint32_t *__restrict__ sz, const uint16_t *__restrict__ bias, int N, int K,
     uint16_t *__restrict__ y, int64_t tile0, int64_t ntiles) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF][STAGE_BYTES];
+    static_assert(BNT == 128 || BNT == 256, "block tile columns");
+    constexpr int BNk = BNT;
+    constexpr int NW = BNk / 32;                 // waves per block
+    constexpr int WN = BNk / 64;                 // waves along n
+    constexpr int XC = 16 / NW;                  // x copies per wave and stage
+    constexpr int B_BYTESk = BNk * KS / 2;       // code tile, packed nibbles
+    constexpr int SZ_BYTESk = 2 * 2 * BNk * 4;   // [group end][s | z][row], 4 B each
+    constexpr int STAGE_BYTESk = A_BYTES + B_BYTESk + SZ_BYTESk;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF][STAGE_BYTESk];
     // scale / zero-point copies per wave and stage (2 bytes each, or one
     // 4-byte pair each in the pre-shuffled layout)
     constexpr int NSZ = (G == 32 && !PK) ? 2 : 1;
-    constexpr int Q = 4 + 1 + NSZ;               // copies per wave and stage
+    constexpr int Q = XC + 1 + NSZ;              // copies per wave and stage
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / WN, wn = wave % WN;
     const int nl = lane & 15, kb = lane >> 4;
     const int ngroups = K / G;
     const int nstages = (K + KS - 1) / KS;
@@ -116,12 +123,12 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
         const int64_t T = ntiles, b = blockIdx.x;
         const int64_t xcd = b & 7, j = b >> 3;
         const int64_t t = tile0 + xcd * (T >> 3) + min(xcd, T & 7) + j;
-        const int64_t mtiles = (M + BM - 1) / BM, ntl = (N + BN - 1) / BN;
+        const int64_t mtiles = (M + BM - 1) / BM, ntl = (N + BNk - 1) / BNk;
         const int64_t gm = min<int64_t>(4, mtiles);
         const int64_t grp = t / (gm * ntl), r = t - grp * gm * ntl;
         const int64_t gsz = min(gm, mtiles - grp * gm);
         m0 = static_cast<int>((grp * gm + r % gsz) * BM);
-        n0 = static_cast<int>((r / gsz) * BN);
+        n0 = static_cast<int>((r / gsz) * BNk);
     }
 
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
@@ -129,10 +136,10 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     // x: copy i of wave w fills rows 8 (4w + i) .. +8; lane l row + l / 8,
     // 16-byte slot l % 8 holding k-piece (l % 8) ^ (row % 8)
 
-    uint32_t a_row[4];
+    uint32_t a_row[XC];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        a_row[i] = static_cast<uint32_t>(min(m0 + (wave * 4 + i) * 8 + (lane >> 3), M - 1));
+    for (int i = 0; i < XC; ++i)
+        a_row[i] = static_cast<uint32_t>(min(m0 + (wave * XC + i) * 8 + (lane >> 3), M - 1));
     // codes: lane l of wave w fills row 32 w + l / 2, 16-byte half l % 2,
     // holding k-half (l % 2) ^ ((row / 8) % 2) (swizzle against conflicts)
     const int b_r = wave * 32 + (lane >> 1);
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
     const uint8_t *b_src = codes + static_cast<int64_t>(min(n0 + b_r, N - 1)) * (K >> 1) + b_half * 16;
 
     // buffer path: descriptors over the block's rows, fixed per-lane offsets
-    const int rows_m = min(BM, M - m0), rows_n = min(BN, N - n0);
+    const int rows_m = min(BM, M - m0), rows_n = min(BNk, N - n0);
     const uint32_t kh = static_cast<uint32_t>(K) >> 1;
     u32x4 xr = {0u, 0u, 0u, 0u}, cr = xr, sr = xr, zr = xr;
     uint32_t xo[2] = {0u, 0u}, co = 0u, so[NSZ > 1 ? NSZ : 1] = {};
@@ -156,43 +163,43 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
         // x copy i: row 8 (4 w + i) + lane / 8, piece (lane % 8) ^ (row / 2 % 8): the
         // row term of copy i is 32 w + 8 i, so copies of equal i % 2 share the
         // swizzle and differ by 8 rows
-        const uint32_t r0 = (wave * 32 + (lane >> 3)) * static_cast<uint32_t>(K);
+        const uint32_t r0 = (wave * 8 * XC + (lane >> 3)) * static_cast<uint32_t>(K);
         xo[0] = (r0 + ((lane & 7) ^ (lane >> 4)) * 8) * 2;
         xo[1] = (r0 + 8 * static_cast<uint32_t>(K) + ((lane & 7) ^ (4 | (lane >> 4))) * 8) * 2;
         co = static_cast<uint32_t>(b_r) * kh + b_half * 16;
         if constexpr (PK) {
-            so[0] = static_cast<uint32_t>((64 * wave + lane) & 127) * ngroups * 4;
+            so[0] = static_cast<uint32_t>((64 * wave + lane) & (BNk - 1)) * ngroups * 4;
         } else {
 #pragma unroll
             for (int d = 0; d < NSZ; ++d)
-                so[d] = static_cast<uint32_t>((64 * (NSZ * wave + d) + lane) & 127) * ngroups * 2;
+                so[d] = static_cast<uint32_t>((64 * (NSZ * wave + d) + lane) & (BNk - 1)) * ngroups * 2;
         }
     }
 
     auto issue = [&](int kt, int buf) {
-        const uint32_t base = lds0 + static_cast<uint32_t>(buf) * STAGE_BYTES;
+        const uint32_t base = lds0 + static_cast<uint32_t>(buf) * STAGE_BYTESk;
         const int k0 = kt * KS;
         if constexpr (BUF) {
             const uint32_t xs = static_cast<uint32_t>(k0) * 2;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < XC; ++i)
                 bcopy16(xr, xo[i & 1] + (i >> 1) * 16 * static_cast<uint32_t>(K) * 2, xs,
-                        base + (wave * 4 + i) * 1024);
+                        base + (wave * XC + i) * 1024);
             bcopy16(cr, co, static_cast<uint32_t>(k0) >> 1, base + A_BYTES + wave * 1024);
             if constexpr (PK) {
-                const int h = (64 * wave) >> 7;
+                const int h = (64 * wave) / BNk;
                 const int k_end = k0 + (G == 32 ? (h + 1) * 32 : KS);
                 const int g = max(0, min(k_end / G - 1, ngroups - 1));
-                bcopy4(sr, so[0], static_cast<uint32_t>(g) * 4, base + A_BYTES + B_BYTES + 256 * wave);
+                bcopy4(sr, so[0], static_cast<uint32_t>(g) * 4, base + A_BYTES + B_BYTESk + 256 * wave);
             } else {
 #pragma unroll
                 for (int d = 0; d < NSZ; ++d) {
                     const int v0 = 64 * (NSZ * wave + d);          // wave-uniform part
-                    const int isz = (v0 >> 7) & 1, h = v0 >> 8;
+                    const int isz = (v0 / BNk) & 1, h = v0 / (2 * BNk);
                     const int k_end = k0 + (G == 32 ? (h + 1) * 32 : KS);
                     const int g = max(0, min(k_end / G - 1, ngroups - 1));
                     bcopy2(isz ? zr : sr, so[d], static_cast<uint32_t>(g) * 2,
-                           base + A_BYTES + B_BYTES + 64 * 4 * (NSZ * wave + d));
+                           base + A_BYTES + B_BYTESk + 64 * 4 * (NSZ * wave + d));
                 }
             }
             return;
@@ -200,10 +207,10 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
         const int kp0 = min(k0 + ((lane & 7) ^ (lane >> 4)) * 8, K - 8);
         const int kp1 = min(k0 + ((lane & 7) ^ (4 | (lane >> 4))) * 8, K - 8);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < XC; ++i)
             copy16(x + (static_cast<uint64_t>(a_row[i]) * static_cast<uint32_t>(K) +
                         static_cast<uint32_t>((i & 1) ? kp1 : kp0)),
-                   base + (wave * 4 + i) * 1024);
+                   base + (wave * XC + i) * 1024);
         // k = min(k0 + 32 * half, K - 32)
         copy16(b_src + min(k0, K - 32 - b_half * 32) / 2, base + A_BYTES + wave * 1024);
         if constexpr (PK) {
@@ -211,23 +218,23 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
             // v = 64 w + lane -> row v % 128, end v / 128 (at G >= 64 both
             // ends are the stage's one group end)
             const int v = 64 * wave + lane;
-            const int row = v & 127, h = v >> 7;
+            const int row = v & (BNk - 1), h = v / BNk;
             const int k_end = k0 + (G == 32 ? (h + 1) * 32 : KS);
             const int g = max(0, min(k_end / G - 1, ngroups - 1));
             copy4(sz + static_cast<int64_t>(min(n0 + row, N - 1)) * ngroups + g,
-                  base + A_BYTES + B_BYTES + 256 * wave);
+                  base + A_BYTES + B_BYTESk + 256 * wave);
         } else {
             // scales / zero-points of the group ends in this stage: value
             // v = 64 (NSZ w + d) + lane -> row v % 128, s|z (v / 128) % 2, end v / 256
 #pragma unroll
             for (int d = 0; d < NSZ; ++d) {
                 const int v = 64 * (NSZ * wave + d) + lane;
-                const int row = v & 127, isz = (v >> 7) & 1, h = v >> 8;
+                const int row = v & (BNk - 1), isz = (v / BNk) & 1, h = v / (2 * BNk);
                 const int k_end = k0 + (G == 32 ? (h + 1) * 32 : KS);
                 const int g = max(0, min(k_end / G - 1, ngroups - 1));
                 const uint16_t *src = (isz ? zeros : scales) +
                                       static_cast<int64_t>(min(n0 + row, N - 1)) * ngroups + g;
-                copy2(src, base + A_BYTES + B_BYTES + 64 * 4 * (NSZ * wave + d));
+                copy2(src, base + A_BYTES + B_BYTESk + 64 * 4 * (NSZ * wave + d));
             }
         }
     };
@@ -303,17 +310,17 @@ __global__ __launch_bounds__(THREADS, 2) void gemm_kernel(
         }
         if constexpr (last) {
             constexpr int h = (G == 32) ? sl : 0;
-            const uint32_t *szp = reinterpret_cast<const uint32_t *>(sb + A_BYTES + B_BYTES);
+            const uint32_t *szp = reinterpret_cast<const uint32_t *>(sb + A_BYTES + B_BYTESk);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 const int c = wn * 64 + nt * 16 + nl;
                 if constexpr (PK) {
-                    const uint32_t pr = szp[h * 128 + c];
+                    const uint32_t pr = szp[h * BNk + c];
                     sv[nt] = bf16_lo(pr);
                     zz[nt] = fmaf(-128.0f, sv[nt], bf16_hi(pr));
                 } else {
-                    sv[nt] = bf16_to_f32(static_cast<uint16_t>(szp[h * 256 + c]));
-                    zz[nt] = fmaf(-128.0f, sv[nt], bf16_to_f32(static_cast<uint16_t>(szp[h * 256 + 128 + c])));
+                    sv[nt] = bf16_to_f32(static_cast<uint16_t>(szp[h * 2 * BNk + c]));
+                    zz[nt] = fmaf(-128.0f, sv[nt], bf16_to_f32(static_cast<uint16_t>(szp[h * 2 * BNk + BNk + c])));
                 }
             }
         }
@@ -384,28 +391,47 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *codes,
                        uint16_t *y, hipStream_t stream) {
     const bool pk = sz != nullptr;
     const bool buf = K < (int64_t(1) << 24);      // 32-bit buffer offsets over 128 rows
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t mtiles = (M + BM - 1) / BM;
+    // 128 x 256 blocks (one per compute unit) when they make one to two waves
+    // of blocks over the chip: measured 4-6 % faster than 128 x 128 blocks on
+    // such layers (Gemma3-12B-shaped q, o and down at M = 2048, plain layout,
+    // G = 64 and 128); about even on layers with more tiles, slower on fewer
+    // tiles, at G = 32 and in the pre-shuffled layout.
+    const int64_t wide_tiles = mtiles * ((N + 255) / 256);
+    const int64_t cus = compute_units();
+    const bool wide = !pk && buf && G >= 64 && wide_tiles * 16 >= cus * 15 && wide_tiles <= 2 * cus;
+    const int64_t bn = wide ? 256 : 128;
+    const int64_t tiles = mtiles * ((N + bn - 1) / bn);
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     // one launch per 2^22 tiles keeps blocks x threads below 2^32
     constexpr int64_t kMaxTiles = int64_t(1) << 22;
     for (int64_t t0 = 0; t0 < tiles; t0 += kMaxTiles) {
         const int64_t nt = min(kMaxTiles, tiles - t0);
         const dim3 grid(static_cast<unsigned>(nt));
-        const dim3 block(THREADS);
+        const dim3 block(static_cast<unsigned>(2 * bn));
 #define W4_GEMM_LAUNCH(GG, PP)                                                               \
     do {                                                                                     \
         if (buf)                                                                             \
-            gemm_kernel<GG, PP, true><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, \
-                                                                  sz, bias, n, k, y, t0, nt); \
+            gemm_kernel<GG, PP, true, 128><<<grid, block, 0, stream>>>(                       \
+                x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);                      \
         else                                                                                 \
-            gemm_kernel<GG, PP, false><<<grid, block, 0, stream>>>(x, m, codes, scales, zeros, \
-                                                                   sz, bias, n, k, y, t0, nt); \
+            gemm_kernel<GG, PP, false, 128><<<grid, block, 0, stream>>>(                      \
+                x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);                      \
     } while (0)
-        switch (G) {
-        case 32: if (pk) W4_GEMM_LAUNCH(32, true); else W4_GEMM_LAUNCH(32, false); break;
-        case 64: if (pk) W4_GEMM_LAUNCH(64, true); else W4_GEMM_LAUNCH(64, false); break;
-        case 128: if (pk) W4_GEMM_LAUNCH(128, true); else W4_GEMM_LAUNCH(128, false); break;
-        default: return hipErrorInvalidValue;
+        if (wide) {
+            if (G == 64)
+                gemm_kernel<64, false, true, 256><<<grid, block, 0, stream>>>(
+                    x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);
+            else
+                gemm_kernel<128, false, true, 256><<<grid, block, 0, stream>>>(
+                    x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);
+        } else {
+            switch (G) {
+            case 32: if (pk) W4_GEMM_LAUNCH(32, true); else W4_GEMM_LAUNCH(32, false); break;
+            case 64: if (pk) W4_GEMM_LAUNCH(64, true); else W4_GEMM_LAUNCH(64, false); break;
+            case 128: if (pk) W4_GEMM_LAUNCH(128, true); else W4_GEMM_LAUNCH(128, false); break;
+            default: return hipErrorInvalidValue;
+            }
         }
 #undef W4_GEMM_LAUNCH
         const hipError_t e = hipGetLastError();

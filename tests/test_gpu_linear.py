@@ -118,6 +118,18 @@ def test_gemm(w4, G, M, N, K):
     run_case(w4, M, N, K, G, bias=(M % 2 == 0), path=gu_path(w4, "GEMM"), seed=3 * N + K + M)
 
 
+# Shapes whose count of 128 x 256 tiles makes one to two waves of blocks over
+# a 256-unit chip (240 .. 512 tiles) run the eight-wave 128 x 256 GEMM block
+# (plain layout, G >= 64): ragged M and N, a one-column tail, bias on half.
+WIDE_SHAPES = [(2000, 4000, 256), (2048, 3840, 384), (2047, 4097, 128), (4000, 2048, 256)]
+
+
+@pytest.mark.parametrize("M,N,K", WIDE_SHAPES)
+@pytest.mark.parametrize("G", [64, 128])
+def test_gemm_wide_blocks(w4, G, M, N, K):
+    run_case(w4, M, N, K, G, bias=(N % 2 == 0), path=gu_path(w4, "GEMM"), seed=N + K + G)
+
+
 @pytest.mark.parametrize("M", [1, 16, 40, 300])
 @pytest.mark.parametrize("G", [32, 128])
 def test_auto_dispatch_outliers(w4, M, G):
