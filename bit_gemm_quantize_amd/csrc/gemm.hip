@@ -109,6 +109,9 @@ __global__ __launch_bounds__(BNT * 2, 2) void gemm_kernel(
     // 4-byte pair each in the pre-shuffled layout)
     constexpr int NSZ = (G == 32 && !PK) ? 2 : 1;
     constexpr int Q = XC + 1 + NSZ;              // copies per wave and stage
+    // At G = 128 a group spans two stages and ends in the odd one: only odd
+    // stages copy scales / zero-points (even stages issue Q - NSZ copies).
+    constexpr bool SZ_ALL = G != 128;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -186,7 +189,9 @@ __global__ __launch_bounds__(BNT * 2, 2) void gemm_kernel(
                 bcopy16(xr, xo[i & 1] + (i >> 1) * 16 * static_cast<uint32_t>(K) * 2, xs,
                         base + (wave * XC + i) * 1024);
             bcopy16(cr, co, static_cast<uint32_t>(k0) >> 1, base + A_BYTES + wave * 1024);
-            if constexpr (PK) {
+            if (!SZ_ALL && !(kt & 1)) {
+                // G = 128: the stage holds no group end, its scale slots are not read
+            } else if constexpr (PK) {
                 const int h = (64 * wave) / BNk;
                 const int k_end = k0 + (G == 32 ? (h + 1) * 32 : KS);
                 const int g = max(0, min(k_end / G - 1, ngroups - 1));
@@ -213,7 +218,9 @@ __global__ __launch_bounds__(BNT * 2, 2) void gemm_kernel(
                    base + (wave * XC + i) * 1024);
         // k = min(k0 + 32 * half, K - 32)
         copy16(b_src + min(k0, K - 32 - b_half * 32) / 2, base + A_BYTES + wave * 1024);
-        if constexpr (PK) {
+        if (!SZ_ALL && !(kt & 1)) {
+            // G = 128: no group end in this stage
+        } else if constexpr (PK) {
             // (s | z << 16) of the group ends in this stage: value
             // v = 64 w + lane -> row v % 128, end v / 128 (at G >= 64 both
             // ends are the stage's one group end)
@@ -348,8 +355,11 @@ __global__ __launch_bounds__(BNT * 2, 2) void gemm_kernel(
         } else {
             slice(buf, par_c, IC<1>{});
         }
-        // stage kt + 1 has landed (stage kt + 2 may still be in flight)
-        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(Q) : "memory");
+        // stage kt + 1 has landed (stage kt + 2, of the same parity as kt,
+        // may still be in flight; past the end the repeated last stage is odd
+        // and issues at least as many copies, so the wait is never short)
+        constexpr int QW = (!SZ_ALL && decltype(par_c)::value == 0) ? Q - NSZ : Q;
+        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(QW) : "memory");
         __syncthreads();
     };
 
