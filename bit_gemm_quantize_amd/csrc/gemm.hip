@@ -402,14 +402,16 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *codes,
     const bool pk = sz != nullptr;
     const bool buf = K < (int64_t(1) << 24);      // 32-bit buffer offsets over 128 rows
     const int64_t mtiles = (M + BM - 1) / BM;
-    // 128 x 256 blocks (one per compute unit) when they make one to two waves
-    // of blocks over the chip: measured 4-6 % faster than 128 x 128 blocks on
-    // such layers (Gemma3-12B-shaped q, o and down at M = 2048, plain layout,
-    // G = 64 and 128); about even on layers with more tiles, slower on fewer
-    // tiles, at G = 32 and in the pre-shuffled layout.
+    // 128 x 256 blocks (one per compute unit) when there are enough of them to
+    // fill the chip (at least 15/16 of a block per compute unit): measured
+    // 2-7 % faster than 128 x 128 blocks on the Gemma3-12B-shaped q, o, gate
+    // and down layers at M = 2048, G = 64 and 128, both layouts (even on
+    // gate at G = 64, pre-shuffled). With fewer tiles (k and v: half a block
+    // per compute unit) and at G = 32 (two scale / zero-point copies per
+    // stage) the 128 x 128 block is faster.
     const int64_t wide_tiles = mtiles * ((N + 255) / 256);
     const int64_t cus = compute_units();
-    const bool wide = !pk && buf && G >= 64 && wide_tiles * 16 >= cus * 15 && wide_tiles <= 2 * cus;
+    const bool wide = buf && G >= 64 && wide_tiles * 16 >= cus * 15;
     const int64_t bn = wide ? 256 : 128;
     const int64_t tiles = mtiles * ((N + bn - 1) / bn);
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
@@ -429,8 +431,14 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *codes,
                 x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);                      \
     } while (0)
         if (wide) {
-            if (G == 64)
+            if (G == 64 && pk)
+                gemm_kernel<64, true, true, 256><<<grid, block, 0, stream>>>(
+                    x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);
+            else if (G == 64)
                 gemm_kernel<64, false, true, 256><<<grid, block, 0, stream>>>(
+                    x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);
+            else if (pk)
+                gemm_kernel<128, true, true, 256><<<grid, block, 0, stream>>>(
                     x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);
             else
                 gemm_kernel<128, false, true, 256><<<grid, block, 0, stream>>>(

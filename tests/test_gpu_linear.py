@@ -118,10 +118,11 @@ def test_gemm(w4, G, M, N, K):
     run_case(w4, M, N, K, G, bias=(M % 2 == 0), path=gu_path(w4, "GEMM"), seed=3 * N + K + M)
 
 
-# Shapes whose count of 128 x 256 tiles makes one to two waves of blocks over
-# a 256-unit chip (240 .. 512 tiles) run the eight-wave 128 x 256 GEMM block
-# (plain layout, G >= 64): ragged M and N, a one-column tail, bias on half.
-WIDE_SHAPES = [(2000, 4000, 256), (2048, 3840, 384), (2047, 4097, 128), (4000, 2048, 256)]
+# Shapes with enough 128 x 256 tiles to fill a 256-unit chip (at least 240)
+# run the eight-wave 128 x 256 GEMM block (G >= 64): ragged M and N, a
+# one-column tail, bias on half; the last one has several blocks per unit.
+WIDE_SHAPES = [(2000, 4000, 256), (2048, 3840, 384), (2047, 4097, 128), (4000, 2048, 256),
+               (3000, 6000, 128)]
 
 
 @pytest.mark.parametrize("M,N,K", WIDE_SHAPES)

@@ -87,6 +87,14 @@ def test_gemm_preshuffled(w4, G, M, N, K):
     run_case(w4, M, N, K, G, bias=(M % 2 == 0), path=w4.W4Path.GEMM, seed=3 * N + K + M)
 
 
+# enough 128 x 256 tiles to fill a 256-unit chip: the eight-wave GEMM block
+# (G >= 64), ragged M and N, a one-column tail, bias on half
+@pytest.mark.parametrize("M,N,K", [(2000, 4000, 256), (2047, 4097, 128), (4000, 2048, 256)])
+@pytest.mark.parametrize("G", [64, 128])
+def test_gemm_preshuffled_wide_blocks(w4, G, M, N, K):
+    run_case(w4, M, N, K, G, bias=(N % 2 == 0), path=w4.W4Path.GEMM, seed=N + K + G)
+
+
 # smallest legal K and fewer output rows than one tile, on both paths
 @pytest.mark.parametrize("path", ["GEMV", "GEMM"])
 @pytest.mark.parametrize("G,M,N,K", _with_groups(
