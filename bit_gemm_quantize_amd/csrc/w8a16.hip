@@ -181,9 +181,12 @@ __global__ __launch_bounds__(THREADS, 2) void w8a16_gemm_kernel(
                    base + (wave * 4 + i) * 1024);
 #pragma unroll
         for (int i = 0; i < 2; ++i) copy16(b_src[i] + k0, base + A_BYTES + (2 * wave + i) * 1024);
-        const int k_end = k0 + (G == 32 ? (sz_h + 1) * 32 : KS);
-        // (at G = 128 an even stage fetches the previous group again, or group 0)
-        copy2(s_src + max(0, min(k_end / G - 1, ngroups - 1)), base + A_BYTES + B_BYTES + 256 * wave);
+        // at G = 128 a group spans two stages and ends in the odd one: only
+        // odd stages fetch scales (their slots in even stages are not read)
+        if (G != 128 || (kt & 1)) {
+            const int k_end = k0 + (G == 32 ? (sz_h + 1) * 32 : KS);
+            copy2(s_src + max(0, min(k_end / G - 1, ngroups - 1)), base + A_BYTES + B_BYTES + 256 * wave);
+        }
     };
 
     f32x4 acc[4][4], accg[4][4], xsg[4];
@@ -263,7 +266,10 @@ __global__ __launch_bounds__(THREADS, 2) void w8a16_gemm_kernel(
         issue(min(kt + 2, nstages - 1), (kt + 2) % NBUF);
         slice(buf, par_c, IC<0>{});
         slice(buf, par_c, IC<1>{});
-        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(Q) : "memory");
+        // stage kt + 2 (same parity as kt; past the end the repeated last
+        // stage is odd and issues at least as many copies) may be in flight
+        constexpr int QW = (G == 128 && decltype(par_c)::value == 0) ? Q - 1 : Q;
+        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(QW) : "memory");
         __syncthreads();
     };
     if constexpr (G == 128) {
