@@ -252,7 +252,10 @@ __global__ __launch_bounds__(THREADS, 2) void w4a8_gemm_kernel(
         for (int i = 0; i < 2; ++i) copy16(a_src[i] + k0, base + (2 * wave + i) * 1024);
         copy16(b_src + k0 / 2, base + A_BYTES + wave * 1024);
         // scales / zero-points of the group ends in this stage: value
-        // v = 64 (NSZ w + d) + lane -> row v % 128, s|z (v / 128) % 2, end v / 256
+        // v = 64 (NSZ w + d) + lane -> row v % 128, s|z (v / 128) % 2, end v / 256;
+        // at G = 128 a group ends in the odd stage of each pair, the only one
+        // whose scale slots are read
+        if (G == 128 && !(kt & 1)) return;
 #pragma unroll
         for (int d = 0; d < NSZ; ++d) {
             const int v = 64 * (NSZ * wave + d) + lane;
@@ -395,7 +398,10 @@ __global__ __launch_bounds__(THREADS, 2) void w4a8_gemm_kernel(
             stage32(buf);
         else
             stage64(buf, par_c);
-        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(Q) : "memory");
+        // stage kt + 2 (same parity as kt; past the end the repeated last
+        // stage is odd and issues at least as many copies) may be in flight
+        constexpr int QW = (G == 128 && decltype(par_c)::value == 0) ? Q - NSZ : Q;
+        asm volatile("s_waitcnt vmcnt(%0)" : : "n"(QW) : "memory");
         __syncthreads();
     };
     if constexpr (G == 128) {
