@@ -5,7 +5,8 @@
 // ("Optimum Quanto": wide accumulation, then dequantization; bias in float).
 //
 // Block tile 128 (m) x BN (n), BN = 128 (four waves in a 2 x 2 grid) or 256
-// (eight waves in a 2 x 4 grid), 64 x 64 per wave.
+// (eight waves in a 2 x 4 grid), 64 x 64 per wave; with at most one 128-wide
+// tile per compute unit, two such groups of four waves split K in one block.
 // K advances in stages of 64 (two 32-wide slices) through three LDS buffers,
 // two stages in flight while one is computed. Every operand reaches LDS by a
 // direct global -> LDS copy issued from asm (16 bytes per lane; scales and
@@ -89,22 +90,27 @@ __device__ __forceinline__ void bcopy2(u32x4 rs, uint32_t voff, uint32_t soff, u
 // 128 * K * 2 < 2^32, i.e. K < 2^24); otherwise 64-bit global addresses
 // recomputed per stage. BNT: block tile columns, 128 or 256 (2 BNT threads;
 // per stage the x tile is shared by BNT / 64 wave columns, so the wider
-// block issues a third fewer copies per MFMA).
-template <int G, bool PK, bool BUF, int BNT>
-__global__ __launch_bounds__(BNT * 2, 2) void gemm_kernel(
+// block issues a third fewer copies per MFMA). KSP = 2 (128-wide tiles,
+// buffer path): two groups of four waves split K in halves inside one block,
+// each with its own stage buffers, and the second group's sums are added
+// through LDS at the end; a grid of at most one tile per compute unit then
+// still runs two waves per SIMD.
+template <int G, bool PK, bool BUF, int BNT, int KSP = 1>
+__global__ __launch_bounds__(BNT * 2 * KSP, 2) void gemm_kernel(
     const uint16_t *__restrict__ x, int M, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     const uint32_t *__restrict__ sz, const uint16_t *__restrict__ bias, int N, int K,
     uint16_t *__restrict__ y, int64_t tile0, int64_t ntiles) {
     static_assert(BNT == 128 || BNT == 256, "block tile columns");
+    static_assert(KSP == 1 || (KSP == 2 && BNT == 128 && BUF), "K split inside the block");
     constexpr int BNk = BNT;
-    constexpr int NW = BNk / 32;                 // waves per block
+    constexpr int NW = BNk / 32;                 // waves per block (per K group)
     constexpr int WN = BNk / 64;                 // waves along n
     constexpr int XC = 16 / NW;                  // x copies per wave and stage
     constexpr int B_BYTESk = BNk * KS / 2;       // code tile, packed nibbles
     constexpr int SZ_BYTESk = 2 * 2 * BNk * 4;   // [group end][s | z][row], 4 B each
     constexpr int STAGE_BYTESk = A_BYTES + B_BYTESk + SZ_BYTESk;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF][STAGE_BYTESk];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[KSP][NBUF][STAGE_BYTESk];
     // scale / zero-point copies per wave and stage (2 bytes each, or one
     // 4-byte pair each in the pre-shuffled layout)
     constexpr int NSZ = (G == 32 && !PK) ? 2 : 1;
@@ -115,11 +121,16 @@ __global__ __launch_bounds__(BNT * 2, 2) void gemm_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // wave: index inside its K group wg (wave-uniform); the group covers
+    // k in [kbase, kbase + K / KSP)
+    const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) % NW);
+    const int wg = KSP == 1 ? 0 : __builtin_amdgcn_readfirstlane((tid >> 6) / NW);
     const int wm = wave / WN, wn = wave % WN;
     const int nl = lane & 15, kb = lane >> 4;
     const int ngroups = K / G;
-    const int nstages = (K + KS - 1) / KS;
+    const int Kg = K / KSP;
+    const int kbase = wg * Kg;
+    const int nstages = (Kg + KS - 1) / KS;
 
     int m0, n0;
     {
@@ -135,7 +146,7 @@ __global__ __launch_bounds__(BNT * 2, 2) void gemm_kernel(
     }
 
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-        (__attribute__((address_space(3))) uint8_t *)&smem[0][0]));
+        (__attribute__((address_space(3))) uint8_t *)&smem[wg][0][0]));
     // x: copy i of wave w fills rows 8 (4w + i) .. +8; lane l row + l / 8,
     // 16-byte slot l % 8 holding k-piece (l % 8) ^ (row % 8)
 
@@ -181,7 +192,7 @@ __global__ __launch_bounds__(BNT * 2, 2) void gemm_kernel(
 
     auto issue = [&](int kt, int buf) {
         const uint32_t base = lds0 + static_cast<uint32_t>(buf) * STAGE_BYTESk;
-        const int k0 = kt * KS;
+        const int k0 = kbase + kt * KS;
         if constexpr (BUF) {
             const uint32_t xs = static_cast<uint32_t>(k0) * 2;
 #pragma unroll
@@ -283,7 +294,7 @@ __global__ __launch_bounds__(BNT * 2, 2) void gemm_kernel(
         constexpr int sl = decltype(sl_c)::value;
         constexpr bool first = G == 128 ? (par == 0 && sl == 0) : (G == 64 ? sl == 0 : true);
         constexpr bool last = G == 128 ? (par == 1 && sl == 1) : (G == 64 ? sl == 1 : true);
-        const uint8_t *sb = &smem[buf][0];
+        const uint8_t *sb = &smem[wg][buf][0];
         // one add per operand and slice: the per-lane offsets are fixed, the
         // m- / n-tile steps are immediates
         const uint8_t *sa = sb + la[sl];
@@ -351,7 +362,7 @@ __global__ __launch_bounds__(BNT * 2, 2) void gemm_kernel(
         issue(min(kt + 2, nstages - 1), (kt + 2) % NBUF);
         slice(buf, par_c, IC<0>{});
         if constexpr (G == 32) {
-            if (kt * KS + 32 < K) slice(buf, par_c, IC<1>{});   // K % 64 == 32: half stage
+            if (kt * KS + 32 < Kg) slice(buf, par_c, IC<1>{});  // K % 64 == 32: half stage
         } else {
             slice(buf, par_c, IC<1>{});
         }
@@ -375,6 +386,25 @@ __global__ __launch_bounds__(BNT * 2, 2) void gemm_kernel(
 
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) epilogue(mt);
+
+    if constexpr (KSP == 2) {
+        // the second K half's sums, through its own (now idle) stage buffers:
+        // 4 waves x 16 tiles x 64 lanes x 16 bytes = 64 KB, lanes contiguous
+        __syncthreads();                        // every copy of the block has landed
+        f32x4 *red = reinterpret_cast<f32x4 *>(&smem[1][0][0]);
+        if (wg == 1) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) red[((wave * 4 + mt) * 4 + nt) * 64 + lane] = acc[mt][nt];
+        }
+        __syncthreads();
+        if (wg == 1) return;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) acc[mt][nt] += red[((wave * 4 + mt) * 4 + nt) * 64 + lane];
+    }
 
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
@@ -414,13 +444,18 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *codes,
     const bool wide = buf && G >= 64 && wide_tiles * 16 >= cus * 15;
     const int64_t bn = wide ? 256 : 128;
     const int64_t tiles = mtiles * ((N + bn - 1) / bn);
+    // at most one 128 x 128 tile per compute unit (k and v of the Gemma3-12B
+    // shapes at M = 2048: one four-wave block per unit, one wave per SIMD):
+    // split K inside eight-wave blocks, each half a multiple of the stage
+    // pair and the group
+    const bool ksplit = !wide && buf && tiles <= cus && K % (2 * (G > KS ? G : KS)) == 0;
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
     // one launch per 2^22 tiles keeps blocks x threads below 2^32
     constexpr int64_t kMaxTiles = int64_t(1) << 22;
     for (int64_t t0 = 0; t0 < tiles; t0 += kMaxTiles) {
         const int64_t nt = min(kMaxTiles, tiles - t0);
         const dim3 grid(static_cast<unsigned>(nt));
-        const dim3 block(static_cast<unsigned>(2 * bn));
+        const dim3 block(static_cast<unsigned>(2 * bn * (ksplit ? 2 : 1)));
 #define W4_GEMM_LAUNCH(GG, PP)                                                               \
     do {                                                                                     \
         if (buf)                                                                             \
@@ -430,7 +465,29 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, const uint8_t *codes,
             gemm_kernel<GG, PP, false, 128><<<grid, block, 0, stream>>>(                      \
                 x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);                      \
     } while (0)
-        if (wide) {
+        if (ksplit) {
+            switch (G) {
+            case 32:
+                if (pk) gemm_kernel<32, true, true, 128, 2><<<grid, block, 0, stream>>>(
+                            x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);
+                else gemm_kernel<32, false, true, 128, 2><<<grid, block, 0, stream>>>(
+                            x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);
+                break;
+            case 64:
+                if (pk) gemm_kernel<64, true, true, 128, 2><<<grid, block, 0, stream>>>(
+                            x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);
+                else gemm_kernel<64, false, true, 128, 2><<<grid, block, 0, stream>>>(
+                            x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);
+                break;
+            case 128:
+                if (pk) gemm_kernel<128, true, true, 128, 2><<<grid, block, 0, stream>>>(
+                            x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);
+                else gemm_kernel<128, false, true, 128, 2><<<grid, block, 0, stream>>>(
+                            x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);
+                break;
+            default: return hipErrorInvalidValue;
+            }
+        } else if (wide) {
             if (G == 64 && pk)
                 gemm_kernel<64, true, true, 256><<<grid, block, 0, stream>>>(
                     x, m, codes, scales, zeros, sz, bias, n, k, y, t0, nt);
