@@ -198,23 +198,32 @@ __device__ __forceinline__ u32x2 codes_to_bytes(uint32_t w) {
                  __builtin_amdgcn_perm(hi, lo, 0x07030602u)};   // q4 q5 q6 q7
 }
 
-template <int G>
-__global__ __launch_bounds__(THREADS, 2) void w4a8_gemm_kernel(
+// KSP = 2: two groups of four waves split K in halves inside one block (own
+// stage buffers), the second group's sums added through LDS at the end; for
+// grids of at most one tile per compute unit, which then still run two waves
+// per SIMD.
+template <int G, int KSP = 1>
+__global__ __launch_bounds__(THREADS * KSP, 2) void w4a8_gemm_kernel(
     const int8_t *__restrict__ x8, const float *__restrict__ sx, int M,
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ zeros, const uint16_t *__restrict__ bias, int N, int K,
     uint16_t *__restrict__ y, int64_t tile0, int64_t ntiles) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF][STAGE_BYTES];
+    static_assert(KSP == 1 || KSP == 2, "K groups");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[KSP][NBUF][STAGE_BYTES];
     constexpr int NSZ = G == 32 ? 2 : 1;         // 2-byte copies per wave and stage
     constexpr int Q = 2 + 1 + NSZ;               // copies per wave and stage
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // wave: index inside its K group wg, which covers [kbase, kbase + K / KSP)
+    const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
+    const int wg = KSP == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);
     const int wm = wave >> 1, wn = wave & 1;
     const int nl = lane & 15, kb = lane >> 4;
     const int ngroups = K / G;
-    const int nstages = K / KS;                  // K % 64 == 0 (checked by the host)
+    const int Kg = K / KSP;
+    const int kbase = wg * Kg;
+    const int nstages = Kg / KS;                 // K % (64 KSP) == 0 (checked by the host)
 
     int m0, n0;
     {
@@ -229,7 +238,7 @@ __global__ __launch_bounds__(THREADS, 2) void w4a8_gemm_kernel(
         n0 = static_cast<int>((r / gsz) * BN);
     }
 
-    const uint32_t lds0 = lds_address(&smem[0][0]);
+    const uint32_t lds0 = lds_address(&smem[wg][0][0]);
     // x8: copy i of wave w fills rows 16 (2w + i) .. +16; lane l: row
     // 16 (2w + i) + l / 4, slot l % 4 holding piece (l % 4) ^ ((row / 4) % 4)
     const int8_t *a_src[2];
@@ -247,7 +256,7 @@ __global__ __launch_bounds__(THREADS, 2) void w4a8_gemm_kernel(
 
     auto issue = [&](int kt, int buf) {
         const uint32_t base = lds0 + static_cast<uint32_t>(buf) * STAGE_BYTES;
-        const int k0 = kt * KS;
+        const int k0 = kbase + kt * KS;
 #pragma unroll
         for (int i = 0; i < 2; ++i) copy16(a_src[i] + k0, base + (2 * wave + i) * 1024);
         copy16(b_src + k0 / 2, base + A_BYTES + wave * 1024);
@@ -308,7 +317,7 @@ __global__ __launch_bounds__(THREADS, 2) void w4a8_gemm_kernel(
         constexpr int par = decltype(par_c)::value;
         constexpr bool first = G == 128 ? par == 0 : true;
         constexpr bool last = G == 128 ? par == 1 : true;
-        const uint8_t *sb = &smem[buf][0];
+        const uint8_t *sb = &smem[wg][buf][0];
         i32x4 a[4], b[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -345,7 +354,7 @@ __global__ __launch_bounds__(THREADS, 2) void w4a8_gemm_kernel(
 
     // G = 32: two 32-wide slices per stage, one group each
     auto stage32 = [&](int buf) {
-        const uint8_t *sb = &smem[buf][0];
+        const uint8_t *sb = &smem[wg][buf][0];
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl) {
             long a[4], b[4];
@@ -417,6 +426,26 @@ __global__ __launch_bounds__(THREADS, 2) void w4a8_gemm_kernel(
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) fold(mt);
 
+    if constexpr (KSP == 2) {
+        // the second K half's sums through the (now idle) stage buffers:
+        // 4 waves x 16 tiles x 64 lanes x 16 bytes = 64 KB, lanes contiguous
+        static_assert(KSP * NBUF * STAGE_BYTES >= 64 * 1024, "reduction space");
+        __syncthreads();                        // every copy of the block has landed
+        f32x4 *red = reinterpret_cast<f32x4 *>(&smem[0][0][0]);
+        if (wg == 1) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) red[((wave * 4 + mt) * 4 + nt) * 64 + lane] = acc[mt][nt];
+        }
+        __syncthreads();
+        if (wg == 1) return;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) acc[mt][nt] += red[((wave * 4 + mt) * 4 + nt) * 64 + lane];
+    }
+
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -470,16 +499,28 @@ hipError_t launch_w4a8_gemm(const int8_t *x8, const float *sx, int64_t M, const 
                             hipStream_t stream) {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    // at most one tile per compute unit: split K inside eight-wave blocks
+    // (each half a multiple of the stage pair and the group)
+    const bool ksplit = tiles <= compute_units() && K % (2 * (G > KS ? G : KS)) == 0;
     constexpr int64_t kMaxTiles = int64_t(1) << 22;
     for (int64_t t0 = 0; t0 < tiles; t0 += kMaxTiles) {
         const int64_t nt = tiles - t0 < kMaxTiles ? tiles - t0 : kMaxTiles;
         const dim3 grid(static_cast<unsigned>(nt));
-        const dim3 block(THREADS);
-        switch (G) {
-        case 32: w4a8_gemm_kernel<32><<<grid, block, 0, stream>>>(x8, sx, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
-        case 64: w4a8_gemm_kernel<64><<<grid, block, 0, stream>>>(x8, sx, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
-        case 128: w4a8_gemm_kernel<128><<<grid, block, 0, stream>>>(x8, sx, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
-        default: return hipErrorInvalidValue;
+        const dim3 block(THREADS * (ksplit ? 2 : 1));
+        if (ksplit) {
+            switch (G) {
+            case 32: w4a8_gemm_kernel<32, 2><<<grid, block, 0, stream>>>(x8, sx, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
+            case 64: w4a8_gemm_kernel<64, 2><<<grid, block, 0, stream>>>(x8, sx, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
+            case 128: w4a8_gemm_kernel<128, 2><<<grid, block, 0, stream>>>(x8, sx, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
+            default: return hipErrorInvalidValue;
+            }
+        } else {
+            switch (G) {
+            case 32: w4a8_gemm_kernel<32><<<grid, block, 0, stream>>>(x8, sx, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
+            case 64: w4a8_gemm_kernel<64><<<grid, block, 0, stream>>>(x8, sx, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
+            case 128: w4a8_gemm_kernel<128><<<grid, block, 0, stream>>>(x8, sx, m, codes, scales, zeros, bias, n, k, y, t0, nt); break;
+            default: return hipErrorInvalidValue;
+            }
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -119,21 +119,30 @@ __device__ __forceinline__ void copy2(const void *g, uint32_t lds) {
                  : : "v"(g), "s"(lds) : "memory", "m0");
 }
 
-template <int G>
-__global__ __launch_bounds__(THREADS, 2) void w8a16_gemm_kernel(
+// KSP = 2: two groups of four waves split K in halves inside one block (own
+// stage buffers), the second group's sums added through LDS at the end; for
+// grids of at most one tile per compute unit, which then still run two waves
+// per SIMD.
+template <int G, int KSP = 1>
+__global__ __launch_bounds__(THREADS * KSP, 2) void w8a16_gemm_kernel(
     const uint16_t *__restrict__ x, int M, const int8_t *__restrict__ q8,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ bias, int N, int K,
     uint16_t *__restrict__ y, int64_t tile0, int64_t ntiles) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NBUF][STAGE_BYTES];
+    static_assert(KSP == 1 || KSP == 2, "K groups");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[KSP][NBUF][STAGE_BYTES];
     constexpr int Q = 4 + 2 + 1;                 // copies per wave and stage
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // wave: index inside its K group wg, which covers [kbase, kbase + K / KSP)
+    const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
+    const int wg = KSP == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 8);
     const int wm = wave >> 1, wn = wave & 1;
     const int nl = lane & 15, kb = lane >> 4;
     const int ngroups = K / G;
-    const int nstages = K / KS;                  // K % 64 == 0 (checked by the host)
+    const int Kg = K / KSP;
+    const int kbase = wg * Kg;
+    const int nstages = Kg / KS;                 // K % (64 KSP) == 0 (checked by the host)
 
     int m0, n0;
     {
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(THREADS, 2) void w8a16_gemm_kernel(
         n0 = static_cast<int>((r / gsz) * BN);
     }
 
-    const uint32_t lds0 = lds_address(&smem[0][0]);
+    const uint32_t lds0 = lds_address(&smem[wg][0][0]);
     // x: copy i of wave w fills rows 8 (4w + i) .. +8; lane l row + l / 8,
     // 16-byte slot l % 8 holding k-piece (l % 8) ^ ((row / 2) % 8)
     uint32_t a_row[4];
@@ -171,7 +180,7 @@ __global__ __launch_bounds__(THREADS, 2) void w8a16_gemm_kernel(
 
     auto issue = [&](int kt, int buf) {
         const uint32_t base = lds0 + static_cast<uint32_t>(buf) * STAGE_BYTES;
-        const int k0 = kt * KS;
+        const int k0 = kbase + kt * KS;
         const int kp0 = k0 + ((lane & 7) ^ (lane >> 4)) * 8;
         const int kp1 = k0 + ((lane & 7) ^ (4 | (lane >> 4))) * 8;
 #pragma unroll
@@ -212,7 +221,7 @@ __global__ __launch_bounds__(THREADS, 2) void w8a16_gemm_kernel(
         constexpr int sl = decltype(sl_c)::value;
         constexpr bool first = G == 128 ? (par == 0 && sl == 0) : (G == 64 ? sl == 0 : true);
         constexpr bool last = G == 128 ? (par == 1 && sl == 1) : (G == 64 ? sl == 1 : true);
-        const uint8_t *sb = &smem[buf][0];
+        const uint8_t *sb = &smem[wg][buf][0];
         bf16x8 a[4], b[4];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -284,6 +293,25 @@ __global__ __launch_bounds__(THREADS, 2) void w8a16_gemm_kernel(
 
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) fold(mt);
+
+    if constexpr (KSP == 2) {
+        // the second K half's sums through its own (now idle) stage buffers:
+        // 4 waves x 16 tiles x 64 lanes x 16 bytes = 64 KB, lanes contiguous
+        __syncthreads();                        // every copy of the block has landed
+        f32x4 *red = reinterpret_cast<f32x4 *>(&smem[1][0][0]);
+        if (wg == 1) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) red[((wave * 4 + mt) * 4 + nt) * 64 + lane] = acc[mt][nt];
+        }
+        __syncthreads();
+        if (wg == 1) return;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) acc[mt][nt] += red[((wave * 4 + mt) * 4 + nt) * 64 + lane];
+    }
 
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
@@ -489,16 +517,28 @@ hipError_t launch_w8a16(const uint16_t *x, int64_t M, const int8_t *q8, const ui
         return hipGetLastError();
     }
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    // at most one tile per compute unit: split K inside eight-wave blocks
+    // (each half a multiple of the stage pair and the group)
+    const bool ksplit = tiles <= compute_units() && K % (2 * (G > KS ? G : KS)) == 0;
     constexpr int64_t kMaxTiles = int64_t(1) << 22;
     for (int64_t t0 = 0; t0 < tiles; t0 += kMaxTiles) {
         const int64_t nt = tiles - t0 < kMaxTiles ? tiles - t0 : kMaxTiles;
         const dim3 grid(static_cast<unsigned>(nt));
-        const dim3 block(THREADS);
-        switch (G) {
-        case 32: w8a16_gemm_kernel<32><<<grid, block, 0, stream>>>(x, m, q8, scales, bias, n, k, y, t0, nt); break;
-        case 64: w8a16_gemm_kernel<64><<<grid, block, 0, stream>>>(x, m, q8, scales, bias, n, k, y, t0, nt); break;
-        case 128: w8a16_gemm_kernel<128><<<grid, block, 0, stream>>>(x, m, q8, scales, bias, n, k, y, t0, nt); break;
-        default: return hipErrorInvalidValue;
+        const dim3 block(THREADS * (ksplit ? 2 : 1));
+        if (ksplit) {
+            switch (G) {
+            case 32: w8a16_gemm_kernel<32, 2><<<grid, block, 0, stream>>>(x, m, q8, scales, bias, n, k, y, t0, nt); break;
+            case 64: w8a16_gemm_kernel<64, 2><<<grid, block, 0, stream>>>(x, m, q8, scales, bias, n, k, y, t0, nt); break;
+            case 128: w8a16_gemm_kernel<128, 2><<<grid, block, 0, stream>>>(x, m, q8, scales, bias, n, k, y, t0, nt); break;
+            default: return hipErrorInvalidValue;
+            }
+        } else {
+            switch (G) {
+            case 32: w8a16_gemm_kernel<32><<<grid, block, 0, stream>>>(x, m, q8, scales, bias, n, k, y, t0, nt); break;
+            case 64: w8a16_gemm_kernel<64><<<grid, block, 0, stream>>>(x, m, q8, scales, bias, n, k, y, t0, nt); break;
+            case 128: w8a16_gemm_kernel<128><<<grid, block, 0, stream>>>(x, m, q8, scales, bias, n, k, y, t0, nt); break;
+            default: return hipErrorInvalidValue;
+            }
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

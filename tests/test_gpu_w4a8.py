@@ -119,7 +119,7 @@ def test_w4a8_rejects_k_not_multiple_of_64(w4):
         w4.w4a8_linear(x8, sx, c, s, z, 32)
 
 
-@pytest.mark.parametrize("layer,G", [("gate", 128), ("q", 32)])
+@pytest.mark.parametrize("layer,G", [("gate", 128), ("q", 32), ("k", 128)])
 def test_gemma3_12b_prefill_w4a8(w4, layer, G):
     N, K = workloads.GEMMA3_12B[layer]
     W = workloads.weight_bits(4, layer)

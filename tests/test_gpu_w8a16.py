@@ -135,7 +135,7 @@ def test_llama3_8b_decode_w8a16(w4, layer):
                     what=f"llama {layer} w8a16", strict=True)
 
 
-@pytest.mark.parametrize("layer", ["gate", "o"])
+@pytest.mark.parametrize("layer", ["gate", "o", "k"])
 def test_gemma3_12b_prefill_w8a16(w4, layer):
     """Full prefill layer, M = 2048, G = 128, sampled rows."""
     N, K = workloads.GEMMA3_12B[layer]
