@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "quantize_kernel_fake": ["quantize.hip", "w4_device.h"],
     "quantize_batch_kernel": ["quantize.hip", "w4_device.h"],
     "gemv1_kernel": ["gemv.hip", "w4_device.h"],
+    "gemv1_kernel_m2": ["gemv.hip", "w4_device.h"],
     "gemv_split_kernel_g32": ["gemv.hip", "w4_device.h"],
     "gemv_split_kernel_g64": ["gemv.hip", "w4_device.h"],
     "gemm_kernel": ["gemm.hip", "w4_device.h"],
@@ -56,7 +57,7 @@ KERNEL_SOURCES = {
     "act_quant_kernel": ["w4a8.hip", "w4_device.h"],
     "read_stream_kernel": ["measure.hip", "w4_device.h"],
 }
-PARTS = ["all", "decode", "gemm", "step", "quantize", "fake", "gemv16", "square", "ps", "w4a8",
+PARTS = ["all", "decode", "gemm", "step", "quantize", "fake", "gemv2", "gemv16", "square", "ps", "w4a8",
          "w8a16", "stream", "copy"]
 
 
@@ -512,8 +513,8 @@ def main():
     if want("decode"):
         comp, step = decode_set(
             torch, w4, dev, layers, 1, G, 0, reps,
-            kernel="gemv1_kernel<128, 4, false, false> (qkv, o, gate_up), "
-                   "gemv1_kernel<128, 4, true, false> (down)",
+            kernel="gemv1_kernel<128, 4, false, false, 1> (qkv, o, gate_up), "
+                   "gemv1_kernel<128, 4, true, false, 1> (down)",
             want_step=True, steps=max(args.steps, 1), warmup=args.warmup)
         out["gemv_m1_g128"] = comp
     if want("decode", "stream"):
@@ -622,6 +623,19 @@ def main():
             "frac": round(rate(tot_b, tot_ms) / HBM_PEAK_GBS, 4),
             "bytes_per_set": tot_b, "set_us": round(tot_ms * 1e3, 3), "per_layer": per}
 
+    # ---- small-batch decode: M = 2 (vector-ALU kernel, both x rows per lane)
+    # and M = 4 (matrix-core split kernel), G = 128 ------------------------------
+    if want("gemv2"):
+        comp, _ = decode_set(
+            torch, w4, dev, layers, 2, G, 3000, reps,
+            kernel="gemv1_kernel<128, 4, false, false, 2> (qkv, o, gate_up), "
+                   "gemv1_kernel<128, 4, true, false, 2> (down)")
+        out["gemv_m2_g128"] = comp
+        comp, _ = decode_set(
+            torch, w4, dev, layers, 4, G, 3000, reps,
+            kernel="gemv_split_kernel<128, 8, false, false>")
+        out["gemv_m4_g128"] = comp
+
     # ---- small-batch decode: M = 16, G = 32 and 64, outlier columns ----------
     if want("gemv16"):
         for Gs in (32, 64):
@@ -670,7 +684,7 @@ def main():
             "quantize": {"kernel": "quantize_kernel<64, false, 2>", "us": round(q_ms * 1e3, 2),
                          "bytes": qb, "GBps": round(rate(qb, q_ms), 1),
                          "frac": round(rate(qb, q_ms) / HBM_PEAK_GBS, 4)},
-            "linear_m1": {"kernel": "gemv1_kernel<64, 4, true, false>", "us": round(m1_ms * 1e3, 2),
+            "linear_m1": {"kernel": "gemv1_kernel<64, 4, true, false, 1>", "us": round(m1_ms * 1e3, 2),
                           "bytes": m1b, "GBps": round(rate(m1b, m1_ms), 1),
                           "frac": round(rate(m1b, m1_ms) / HBM_PEAK_GBS, 4)},
             "linear_m32768": {"kernel": "gemm_kernel<64, false, true, 256>", "ms": round(big_ms, 3),
@@ -681,7 +695,7 @@ def main():
     # ---- pre-shuffled layout: decode M = 1 and prefill M = 2048 --------------
     if want("ps"):
         comp, _ = decode_set(torch, w4, dev, layers, 1, G, 0, reps, ps=True,
-                             kernel="gemv1_kernel<128, 4, false|true, true>")
+                             kernel="gemv1_kernel<128, 4, false|true, true, 1>")
         out["gemv_m1_g128_ps"] = comp
         out["gemm_m2048_g128_ps"] = prefill_set(torch, w4, dev, glayers, 2048, G, reps, ps=True,
                                                 kernel="gemm_kernel<128, true, true, 128|256> (128 x 256 blocks except k, v)")
@@ -819,7 +833,8 @@ def main():
         del a, b
 
     # ---- report --------------------------------------------------------------
-    for comp, kern in (("gemv_m1_g128", "gemv1_kernel"), ("gemm_m2048_g128", "gemm_kernel"),
+    for comp, kern in (("gemv_m1_g128", "gemv1_kernel"), ("gemv_m2_g128", "gemv1_kernel_m2"),
+                       ("gemm_m2048_g128", "gemm_kernel"),
                        ("quantize_g128", "quantize_kernel"), ("fake_quant_g32", "quantize_kernel_fake"),
                        ("quantize_batch_g128", "quantize_batch_kernel"),
                        ("gemm_m2048_g128_ps", "gemm_kernel_ps"),

@@ -902,25 +902,28 @@ hipError_t allow_large_lds(Kern kern) {
     return e;
 }
 
-// ------------------------------------------------------------------ M = 1
-// Decode GEMV for a single activation row, with the products on the vector
-// ALUs (bf16 pair dot products accumulated in float32). At M = 1 the
-// matrix-core layout above carries 15 padding rows and ties each load to 16
-// rows x 64 bytes; here a wave takes R consecutive output rows and one
-// 2048-wide K segment, lane l covering k = 2048 s + 32 l .. +32 (16 code
-// bytes), so every load of a row is 1 KB contiguous and the blocks of a
-// launch sweep memory in order. A block holds RG row groups x NSB segment
+// ---------------------------------------------------------- M = 1, 2
+// Decode GEMV for one or two activation rows, with the products on the
+// vector ALUs (bf16 pair dot products accumulated in float32). At such M
+// the matrix-core layout below carries 14 or 15 padding rows and ties each
+// load to 16 rows x 64 bytes; here a wave takes R consecutive output rows
+// and one 2048-wide K segment, lane l covering k = 2048 s + 32 l .. +32 (16
+// code bytes), so every load of a row is 1 KB contiguous and the blocks of
+// a launch sweep memory in order. A block holds RG row groups x NSB segment
 // waves; a wave whose row needs more than NSB segments takes every NSB-th.
-//   * x: the lane's 32 values stay in registers for all R rows. Loaded
-//     directly (4 x 16 bytes per lane), or (XLDS) as four contiguous 1 KB
-//     runs passed through a per-wave LDS slab, which pays once the row spans
-//     several segments. Plain codes expand in the interleaved order
-//     (0,4), (1,5), (2,6), (3,7), so x is permuted to match; pre-shuffled
-//     codes expand in natural order.
-//   * per row and lane (its 32 codes lie in one group), in float32:
+//   * x: the lane's 32 values of each of the MR activation rows stay in
+//     registers for all R weight rows. Loaded directly (4 x 16 bytes per lane and row), or
+//     (XLDS) as four contiguous 1 KB runs per row passed through a per-wave
+//     LDS slab one row at a time, which pays once the row spans several
+//     segments. Plain codes expand in the interleaved order (0,4), (1,5),
+//     (2,6), (3,7), so x is permuted to match; pre-shuffled codes expand in
+//     natural order. Each code word is expanded once and meets all MR rows.
+//   * per weight row, activation row and lane (its 32 codes lie in one
+//     group), in float32:
 //       v += s * sum x (128 + q) + (z - 128 s) * sum x.
-//   * the R partial sums are reduced across the wave with lane swaps and
-//     DPP, then across the segment waves of the row through LDS.
+//   * the R partial sums of each activation row are reduced across the wave
+//     with lane swaps and DPP, then across the segment waves of the row
+//     through LDS.
 constexpr int GV1_MAX_WAVES = 16;         // waves per block (1024 threads)
 constexpr int GV1_SEG = 2048;             // k per wave segment
 
@@ -935,19 +938,20 @@ __device__ __forceinline__ float reduce_rows4(float v0, float v1, float v2, floa
     return group_sum<16>(__uint_as_float(c[0]) + __uint_as_float(c[1]));
 }
 
-template <int G, int R, bool XLDS, bool PK>
+template <int G, int R, bool XLDS, bool PK, int MR>
 __global__ __launch_bounds__(GV1_MAX_WAVES * 64) void gemv1_kernel(
     const uint16_t *__restrict__ x, const uint8_t *__restrict__ codes,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     const uint32_t *__restrict__ sz, const uint16_t *__restrict__ bias, int N, int K,
     uint16_t *__restrict__ y, int nseg, int nsb, int rg) {
     static_assert(R % 4 == 0, "rows per wave");
+    static_assert(MR == 1 || MR == 2, "activation rows");
     constexpr int GPS = GV1_SEG / G;          // groups per segment: 16, 32, 64
     constexpr int P = R * GPS / 64;           // scale / zero-point values per lane
-    // dynamic LDS: partial row sums [waves][R] f32, then (XLDS) 4 KB per wave
+    // dynamic LDS: partial row sums [waves][R][MR] f32, then (XLDS) 4 KB per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t g1_smem[];
     float *red = reinterpret_cast<float *>(g1_smem);
-    uint8_t *g1_slab = g1_smem + GV1_MAX_WAVES * R * 4;
+    uint8_t *g1_slab = g1_smem + GV1_MAX_WAVES * R * MR * 4;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -962,30 +966,40 @@ __global__ __launch_bounds__(GV1_MAX_WAVES * 64) void gemv1_kernel(
         PK ? buf_rsrc(sz + row0 * ngroups, rows * ngroups * 4)
            : buf_rsrc(scales + row0 * ngroups, rows * ngroups * 2);
     const __amdgpu_buffer_rsrc_t zrs = PK ? srs : buf_rsrc(zeros + row0 * ngroups, rows * ngroups * 2);
-    const __amdgpu_buffer_rsrc_t xrs = buf_rsrc(x, static_cast<uint32_t>(K) * 2);
+    // one resource per activation row
+    __amdgpu_buffer_rsrc_t xrs[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+        xrs[m] = buf_rsrc(x + static_cast<int64_t>(m) * K, static_cast<uint32_t>(K) * 2);
     const uint32_t ones = 0x3F803F80u;      // bf16 pair (1, 1)
     const Unpack128 uc = unpack128_consts();
 
-    float v[R];
+    float v[R][MR];
 #pragma unroll
-    for (int r = 0; r < R; ++r) v[r] = 0.f;
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MR; ++m) v[r][m] = 0.f;
 
     for (int seg = sw; seg < nseg; seg += nsb) {
         const uint32_t k0 = static_cast<uint32_t>(seg) * GV1_SEG + 32u * lane;
         const bool ok = k0 < static_cast<uint32_t>(K);
         // x first (needed first), then scales / zero-points, then the codes
-        u32x4 xv[4];
-        if constexpr (XLDS) {
+        u32x4 xv[MR][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {   // piece p = lane + 64 i of the segment (8 k)
-                const uint32_t kx = static_cast<uint32_t>(seg) * GV1_SEG + 8u * (lane + 64 * i);
-                xv[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                    xrs, kx < static_cast<uint32_t>(K) ? kx * 2 : OOB, 0, 0);
+        for (int m = 0; m < MR; ++m) {
+            if constexpr (XLDS) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {   // piece p = lane + 64 i of the segment (8 k)
+                    const uint32_t kx = static_cast<uint32_t>(seg) * GV1_SEG + 8u * (lane + 64 * i);
+                    xv[m][i] = __builtin_amdgcn_raw_buffer_load_b128(
+                        xrs[m], kx < static_cast<uint32_t>(K) ? kx * 2 : OOB, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    xv[m][i] = __builtin_amdgcn_raw_buffer_load_b128(xrs[m], ok ? (k0 + 8 * i) * 2 : OOB,
+                                                                     0, 0);
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                xv[i] = __builtin_amdgcn_raw_buffer_load_b128(xrs, ok ? (k0 + 8 * i) * 2 : OOB, 0, 0);
         }
         // (issued before the codes: loads complete in order, so each row can
         // be finished as soon as its own codes arrive)
@@ -1017,39 +1031,57 @@ __global__ __launch_bounds__(GV1_MAX_WAVES * 64) void gemv1_kernel(
                                                          W4_CPOL_STREAM);
         if constexpr (XLDS) {
             // piece p -> slot 4 (p / 4) + ((p % 4) ^ ((p / 16) % 4)): the four
-            // reads below (lane l: pieces 4 l .. 4 l + 3) are conflict-free
+            // reads below (lane l: pieces 4 l .. 4 l + 3) are conflict-free.
+            // One activation row at a time through the same slab (a wave's
+            // LDS operations complete in issue order).
             u32x4 *slab = reinterpret_cast<u32x4 *>(g1_slab) + wave * 256;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int p = lane + 64 * i;
-                slab[4 * (p >> 2) + ((p & 3) ^ ((p >> 4) & 3))] = PK ? xv[i] : interleave8_bf16(xv[i]);
-            }
-            __builtin_amdgcn_wave_barrier();
+            for (int m = 0; m < MR; ++m) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xv[i] = slab[4 * lane + (i ^ ((lane >> 2) & 3))];
+                for (int i = 0; i < 4; ++i) {
+                    const int p = lane + 64 * i;
+                    slab[4 * (p >> 2) + ((p & 3) ^ ((p >> 4) & 3))] =
+                        PK ? xv[m][i] : interleave8_bf16(xv[m][i]);
+                }
+                __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xv[m][i] = slab[4 * lane + (i ^ ((lane >> 2) & 3))];
+                __builtin_amdgcn_wave_barrier();
+            }
         } else if constexpr (!PK) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xv[i] = interleave8_bf16(xv[i]);
-        }
-        float xs = 0.f;
+            for (int m = 0; m < MR; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xs = dot2_bf16(xv[i].x, ones, xs);
-            xs = dot2_bf16(xv[i].y, ones, xs);
-            xs = dot2_bf16(xv[i].z, ones, xs);
-            xs = dot2_bf16(xv[i].w, ones, xs);
+                for (int i = 0; i < 4; ++i) xv[m][i] = interleave8_bf16(xv[m][i]);
+        }
+        float xs[MR];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            xs[m] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xs[m] = dot2_bf16(xv[m][i].x, ones, xs[m]);
+                xs[m] = dot2_bf16(xv[m][i].y, ones, xs[m]);
+                xs[m] = dot2_bf16(xv[m][i].z, ones, xs[m]);
+                xs[m] = dot2_bf16(xv[m][i].w, ones, xs[m]);
+            }
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            float p0 = 0.f, p1 = 0.f;
+            float p0[MR], p1[MR];
+#pragma unroll
+            for (int m = 0; m < MR; ++m) p0[m] = p1[m] = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 uint32_t w[4];
                 unpack8_bias128_il(q[r][i], w, uc);   // pairs (q0,q4).. plain, (q0,q1).. pre-shuffled
-                p0 = dot2_bf16(xv[i].x, w[0], p0);
-                p1 = dot2_bf16(xv[i].y, w[1], p1);
-                p0 = dot2_bf16(xv[i].z, w[2], p0);
-                p1 = dot2_bf16(xv[i].w, w[3], p1);
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    p0[m] = dot2_bf16(xv[m][i].x, w[0], p0[m]);
+                    p1[m] = dot2_bf16(xv[m][i].y, w[1], p1[m]);
+                    p0[m] = dot2_bf16(xv[m][i].z, w[2], p0[m]);
+                    p1[m] = dot2_bf16(xv[m][i].w, w[3], p1[m]);
+                }
             }
             // this lane's group: lane / (G / 32); source lane of row r's value
             const int src = ((r * GPS) % 64 + lane / (G / 32)) * 4;
@@ -1066,35 +1098,44 @@ __global__ __launch_bounds__(GV1_MAX_WAVES * 64) void gemv1_kernel(
                     __builtin_amdgcn_ds_bpermute(src, static_cast<int>(zreg[(r * GPS) / 64]))));
             }
             const float zz = fmaf(-128.0f, s, z);
-            v[r] = fmaf(s, p0 + p1, fmaf(zz, xs, v[r]));
+#pragma unroll
+            for (int m = 0; m < MR; ++m) v[r][m] = fmaf(s, p0[m] + p1[m], fmaf(zz, xs[m], v[r][m]));
         }
     }
 #pragma unroll
-    for (int r = 0; r < R; r += 4) {
-        const float t = reduce_rows4(v[r], v[r + 1], v[r + 2], v[r + 3]);
-        if ((lane & 15) == 0) red[wave * R + r + (lane >> 4)] = t;
-    }
+    for (int m = 0; m < MR; ++m)
+#pragma unroll
+        for (int r = 0; r < R; r += 4) {
+            const float t = reduce_rows4(v[r][m], v[r + 1][m], v[r + 2][m], v[r + 3][m]);
+            if ((lane & 15) == 0) red[(wave * R + r + (lane >> 4)) * MR + m] = t;
+        }
     __syncthreads();
     const int t = threadIdx.x;
-    if (t < rg * R) {
-        const int rr = t / R, r = t % R;
+    if (t < rg * R * MR) {
+        const int m = t % MR, rr = t / (R * MR), r = (t / MR) % R;
         const int64_t row = (static_cast<int64_t>(blockIdx.x) * rg + rr) * R + r;
         if (row < N) {
             float sum = 0.f;
-            for (int w = 0; w < nsb; ++w) sum += red[(rr * nsb + w) * R + r];
+            for (int w = 0; w < nsb; ++w) sum += red[((rr * nsb + w) * R + r) * MR + m];
             if (bias) sum += bf16_to_f32(bias[row]);
-            y[row] = static_cast<uint16_t>(f32_to_bf16_rne(sum));
+            y[static_cast<int64_t>(m) * N + row] = static_cast<uint16_t>(f32_to_bf16_rne(sum));
         }
     }
 }
 
-// M = 1: four rows per wave; x loaded directly while a row spans at most two
-// segments (K <= 4096), through LDS beyond (measured on the Llama-3-8B decode
-// shapes and the 32768-square layer; eight rows per wave were slower).
-template <int G, bool PK>
-hipError_t launch_gemv1(const uint16_t *x, const uint8_t *codes, const uint16_t *scales,
-                        const uint16_t *zeros, const uint32_t *sz, const uint16_t *bias,
-                        int N, int K, uint16_t *y, hipStream_t stream) {
+// M <= GV1_MAX_M: four rows per wave; x loaded directly while a row spans at
+// most two segments (K <= 4096), through LDS beyond (measured on the
+// Llama-3-8B decode shapes and the 32768-square layer; eight rows per wave
+// were slower at M = 1). At M = 2 the kernel beats the matrix-core split
+// kernel on every decode layer (4-28 %); four activation rows per lane
+// (M = 3, 4) made it vector-bound and slower on the wide layers, so those
+// stay on the split kernel.
+constexpr int GV1_MAX_M = 2;
+
+template <int G, bool PK, int MR>
+hipError_t launch_gemv1_mr(const uint16_t *x, const uint8_t *codes, const uint16_t *scales,
+                           const uint16_t *zeros, const uint32_t *sz, const uint16_t *bias,
+                           int N, int K, uint16_t *y, hipStream_t stream) {
     const int nseg = (K + GV1_SEG - 1) / GV1_SEG;
     const int nsb = nseg < GV1_MAX_WAVES ? nseg : GV1_MAX_WAVES;
     const int rg = nsb >= 4 ? 1 : 4 / nsb;             // about four waves per block
@@ -1103,18 +1144,26 @@ hipError_t launch_gemv1(const uint16_t *x, const uint8_t *codes, const uint16_t 
     const int64_t rows_per_block = static_cast<int64_t>(rg) * R;
     const unsigned blocks = static_cast<unsigned>((N + rows_per_block - 1) / rows_per_block);
     const dim3 block(static_cast<unsigned>(rg * nsb * 64));
-    const size_t red_bytes = static_cast<size_t>(GV1_MAX_WAVES) * R * 4;
+    const size_t red_bytes = static_cast<size_t>(GV1_MAX_WAVES) * R * MR * 4;
     if (xlds) {
-        const hipError_t e = allow_large_lds(gemv1_kernel<G, R, true, PK>);
+        const hipError_t e = allow_large_lds(gemv1_kernel<G, R, true, PK, MR>);
         if (e != hipSuccess) return e;
-        gemv1_kernel<G, R, true, PK><<<dim3(blocks), block,
-                                       red_bytes + static_cast<size_t>(rg * nsb) * 4096, stream>>>(
+        gemv1_kernel<G, R, true, PK, MR><<<dim3(blocks), block,
+                                           red_bytes + static_cast<size_t>(rg * nsb) * 4096, stream>>>(
             x, codes, scales, zeros, sz, bias, N, K, y, nseg, nsb, rg);
     } else {
-        gemv1_kernel<G, R, false, PK><<<dim3(blocks), block, red_bytes, stream>>>(
+        gemv1_kernel<G, R, false, PK, MR><<<dim3(blocks), block, red_bytes, stream>>>(
             x, codes, scales, zeros, sz, bias, N, K, y, nseg, nsb, rg);
     }
     return hipGetLastError();
+}
+
+template <int G, bool PK>
+hipError_t launch_gemv1(const uint16_t *x, int M, const uint8_t *codes, const uint16_t *scales,
+                        const uint16_t *zeros, const uint32_t *sz, const uint16_t *bias,
+                        int N, int K, uint16_t *y, hipStream_t stream) {
+    if (M == 1) return launch_gemv1_mr<G, PK, 1>(x, codes, scales, zeros, sz, bias, N, K, y, stream);
+    return launch_gemv1_mr<G, PK, 2>(x, codes, scales, zeros, sz, bias, N, K, y, stream);
 }
 
 // The split kernel stages x through LDS copies (NAT) from this M on.
@@ -1213,7 +1262,7 @@ hipError_t launch_gemv_g(const uint16_t *x, int M, const uint8_t *codes,
                          const uint16_t *bias, int N, int K, uint16_t *y,
                          hipStream_t stream) {
     const int ntiles = (N + 15) / 16;
-    if (M == 1) return launch_gemv1<G, PK>(x, codes, scales, zeros, sz, bias, N, K, y, stream);
+    if (M <= GV1_MAX_M) return launch_gemv1<G, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
     if (M <= GV_SPLIT_MAX_M && split_lds_bytes(M, K, G) <= max_lds_per_block()) {
         return launch_split<G, PK>(x, M, codes, scales, zeros, sz, bias, N, K, y, stream);
     }

@@ -65,7 +65,7 @@ def _with_groups(cases, groups=(32, 64, 128)):
 
 
 @pytest.mark.parametrize("G,M,N,K", _with_groups(
-    [(M, N, K) for M in (1, 2, 3, 5, 8, 15, 16) for N, K in GEMV_SHAPES]))
+    [(M, N, K) for M in (1, 2, 3, 4, 5, 8, 15, 16) for N, K in GEMV_SHAPES]))
 def test_gemv(w4, G, M, N, K):
     run_case(w4, M, N, K, G, bias=(M % 2 == 1), path=gu_path(w4, "GEMV"), seed=N + K + M)
 
@@ -93,7 +93,12 @@ LONG_K_CASES = [(16, 40, 10240, 32), (16, 40, 10240, 64), (16, 40, 10240, 128),
                 # than two 2048-wide segments; past 16 segments a wave takes
                 # several (K = 40960: 20 segments)
                 (1, 40, 10240, 32), (1, 19, 10048, 64), (1, 24, 14336, 128),
-                (1, 20, 40960, 64), (1, 9, 6144 + 96, 32)]
+                (1, 20, 40960, 64), (1, 9, 6144 + 96, 32),
+                # M = 2 on the same kernel: both x rows through the slab, one
+                # at a time (K = 36864: 18 segments, so some waves take two)
+                (2, 21, 14336, 128), (2, 11, 36864, 128),
+                # M = 3, 4 with long rows on the split and direct kernels
+                (3, 17, 18432, 32), (4, 20, 40960, 64), (4, 13, 6144 + 64, 64)]
 
 
 @pytest.mark.parametrize("M,N,K,G", LONG_K_CASES)

@@ -68,7 +68,8 @@ def test_repack_bit_exact(w4, N, K, G):
 # decode kernels: register-staged x (M < 5), LDS-copied x (M >= 5), x read
 # from L2 (x too long for LDS, K % 128 == 0), phased staging (otherwise)
 GEMV_CASES = [(1, 33, 256), (3, 100, 96 * 2), (5, 48, 320), (16, 200, 1024),
-              (16, 40, 10240), (16, 40, 10016), (8, 17, 4096 + 128)]
+              (16, 40, 10240), (16, 40, 10016), (8, 17, 4096 + 128),
+              (2, 40, 10240), (4, 17, 4096 + 128), (4, 24, 14336)]
 
 
 def _with_groups(cases, groups=(32, 64, 128)):
