@@ -51,7 +51,7 @@ KERNEL_SOURCES = {
     "gemm_kernel": ["gemm.hip", "w4_device.h"],
     "gemm_kernel_ps": ["gemm.hip", "w4_device.h"],
     "quantize8_kernel": ["w8a16.hip", "w4_device.h"],
-    "w8a16_gemv_kernel": ["w8a16.hip", "w4_device.h"],
+    "w8a16_gemv_rows_kernel": ["w8a16_rows.hip", "w4_device.h"],
     "w8a16_gemm_kernel": ["w8a16.hip", "w4_device.h"],
     "w4a8_gemm_kernel": ["w4a8.hip", "w4_device.h"],
     "act_quant_kernel": ["w4a8.hip", "w4_device.h"],
@@ -785,7 +785,7 @@ def main():
             tot_q_b += bq
             del copies
         out["w8a16_gemv_m1"] = {
-            "kernel": "w8a16_gemv_kernel<128>", "bound": "hbm",
+            "kernel": "w8a16_gemv_rows_kernel<128, 1>", "bound": "hbm",
             "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
             "achieved_GBps": round(rate(tot_b, tot_ms), 1),
             "frac": round(rate(tot_b, tot_ms) / HBM_PEAK_GBS, 4), "bytes_per_set": tot_b,
@@ -838,7 +838,7 @@ def main():
                        ("quantize_g128", "quantize_kernel"), ("fake_quant_g32", "quantize_kernel_fake"),
                        ("quantize_batch_g128", "quantize_batch_kernel"),
                        ("gemm_m2048_g128_ps", "gemm_kernel_ps"),
-                       ("w8a16_gemv_m1", "w8a16_gemv_kernel"), ("quantize8_g128", "quantize8_kernel"),
+                       ("w8a16_gemv_m1", "w8a16_gemv_rows_kernel"), ("quantize8_g128", "quantize8_kernel"),
                        ("w8a16_gemm_m2048", "w8a16_gemm_kernel"),
                        ("w4a8_gemm_m2048_g128", "w4a8_gemm_kernel"),
                        ("gemv_m16_g32", "gemv_split_kernel_g32"),

@@ -263,8 +263,10 @@ w4_status w8a16_linear(const uint16_t *x, int64_t M, const int8_t *codes8,
     if (overlap(y, ybytes, x, 2 * M * K) || overlap(y, ybytes, codes8, N * K) ||
         overlap(y, ybytes, scales, 2 * N * (K / G)) || overlap(y, ybytes, bias, 2 * N))
         return W4_ERR_ALIAS;
-    const hipError_t e = w4::launch_w8a16(x, M, codes8, scales, bias, N, K, static_cast<int>(G),
-                                          y, stream);
+    const hipError_t e =
+        M <= w4::W8_ROWS_MAX_M && K <= w4::W8_ROWS_MAX_K
+            ? w4::launch_w8a16_rows(x, M, codes8, scales, bias, N, K, static_cast<int>(G), y, stream)
+            : w4::launch_w8a16(x, M, codes8, scales, bias, N, K, static_cast<int>(G), y, stream);
     return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
 

@@ -98,7 +98,12 @@ def run_linear(w4, M, N, K, G, bias, seed):
     for M, N, K in [(1, 64, 128), (1, 300, 1024), (5, 17, 384), (16, 130, 3840),
                     (17, 300, 256), (129, 130, 512), (257, 257, 1024), (40, 96, 3840),
                     # fewer output rows than one 16-row tile, smallest K
-                    (1, 1, 64), (3, 7, 64), (16, 15, 64), (20, 7, 64)]
+                    (1, 1, 64), (3, 7, 64), (16, 15, 64), (20, 7, 64),
+                    # M <= 2 on the vector-ALU kernel: 1024-wide segments,
+                    # a partial last segment, and more than 16 segments per
+                    # row (a wave takes several)
+                    (2, 7, 64), (2, 33, 3840), (1, 19, 1024 + 64), (2, 13, 5120 + 192),
+                    (1, 40, 16384 + 1024), (2, 9, 18432)]
     for G in (32, 64, 128) if K % G == 0])
 def test_w8a16_linear(w4, G, M, N, K):
     run_linear(w4, M, N, K, G, bias=(M % 2 == 1), seed=7 * N + K + M + G)
