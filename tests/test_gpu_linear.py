@@ -101,6 +101,15 @@ LONG_K_CASES = [(16, 40, 10240, 32), (16, 40, 10240, 64), (16, 40, 10240, 128),
                 (3, 17, 18432, 32), (4, 20, 40960, 64), (4, 13, 6144 + 64, 64)]
 
 
+# Two activation rows with a bias: every row of y gets the bias (the other
+# parametrisations give odd M the bias), on both x paths of the M <= 2
+# kernel (direct loads at K <= 4096, the LDS slab beyond) and both layouts'
+# group sizes.
+@pytest.mark.parametrize("G,N,K", [(32, 37, 2048), (128, 64, 4096), (64, 21, 10240), (128, 9, 14336)])
+def test_gemv_two_rows_with_bias(w4, G, N, K):
+    run_case(w4, 2, N, K, G, bias=True, path=gu_path(w4, "GEMV"), seed=3 * N + K)
+
+
 @pytest.mark.parametrize("M,N,K,G", LONG_K_CASES)
 def test_gemv_long_k(w4, M, N, K, G):
     run_case(w4, M, N, K, G, bias=(K % 3 == 1), path=gu_path(w4, "GEMV"), seed=M + N + K)

@@ -109,6 +109,13 @@ def test_w8a16_linear(w4, G, M, N, K):
     run_linear(w4, M, N, K, G, bias=(M % 2 == 1), seed=7 * N + K + M + G)
 
 
+# Two activation rows with a bias on the vector-ALU kernel (the shared
+# parametrisation gives only odd M a bias).
+@pytest.mark.parametrize("G,N,K", [(32, 37, 2048), (128, 64, 4096), (64, 21, 14336)])
+def test_w8a16_two_rows_with_bias(w4, G, N, K):
+    run_linear(w4, 2, N, K, G, bias=True, seed=5 * N + K)
+
+
 def test_w8a16_empty_batch(w4):
     q = torch.zeros((16, 128), dtype=torch.int8, device="cuda")
     s = torch.zeros((16, 4), dtype=torch.bfloat16, device="cuda")
