@@ -50,7 +50,7 @@ hipError_t launch_w8a16(const uint16_t *x, int64_t M, const int8_t *q8, const ui
                         hipStream_t stream);
 // Its decode kernel on the vector ALUs for 1 <= M <= W8_ROWS_MAX_M and
 // K <= W8_ROWS_MAX_K (32-bit buffer offsets); hipErrorInvalidValue otherwise.
-constexpr int64_t W8_ROWS_MAX_M = 2;
+constexpr int64_t W8_ROWS_MAX_M = 4;
 constexpr int64_t W8_ROWS_MAX_K = int64_t(1) << 24;
 hipError_t launch_w8a16_rows(const uint16_t *x, int64_t M, const int8_t *q8,
                              const uint16_t *scales, const uint16_t *bias, int64_t N, int64_t K,

@@ -99,21 +99,23 @@ def run_linear(w4, M, N, K, G, bias, seed):
                     (17, 300, 256), (129, 130, 512), (257, 257, 1024), (40, 96, 3840),
                     # fewer output rows than one 16-row tile, smallest K
                     (1, 1, 64), (3, 7, 64), (16, 15, 64), (20, 7, 64),
-                    # M <= 2 on the vector-ALU kernel: 1024-wide segments,
-                    # a partial last segment, and more than 16 segments per
+                    # M <= 4 on the vector-ALU kernel: 1024-wide segments,
+                    # a partial last segment, and more than 8 segments per
                     # row (a wave takes several)
                     (2, 7, 64), (2, 33, 3840), (1, 19, 1024 + 64), (2, 13, 5120 + 192),
-                    (1, 40, 16384 + 1024), (2, 9, 18432)]
+                    (1, 40, 16384 + 1024), (2, 9, 18432), (4, 33, 3840), (3, 19, 1024 + 64),
+                    (4, 9, 18432), (3, 5, 9216)]
     for G in (32, 64, 128) if K % G == 0])
 def test_w8a16_linear(w4, G, M, N, K):
     run_linear(w4, M, N, K, G, bias=(M % 2 == 1), seed=7 * N + K + M + G)
 
 
-# Two activation rows with a bias on the vector-ALU kernel (the shared
-# parametrisation gives only odd M a bias).
+# Even M with a bias on the vector-ALU kernel (the shared parametrisation
+# gives only odd M a bias).
+@pytest.mark.parametrize("M", [2, 4])
 @pytest.mark.parametrize("G,N,K", [(32, 37, 2048), (128, 64, 4096), (64, 21, 14336)])
-def test_w8a16_two_rows_with_bias(w4, G, N, K):
-    run_linear(w4, 2, N, K, G, bias=True, seed=5 * N + K)
+def test_w8a16_even_rows_with_bias(w4, M, G, N, K):
+    run_linear(w4, M, N, K, G, bias=True, seed=5 * N + K + M)
 
 
 def test_w8a16_empty_batch(w4):
