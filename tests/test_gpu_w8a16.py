@@ -118,6 +118,28 @@ def test_w8a16_even_rows_with_bias(w4, M, G, N, K):
     run_linear(w4, M, N, K, G, bias=True, seed=5 * N + K + M)
 
 
+def _random_cases(n=24, seed=808):
+    """Seeded shapes: ragged N, M across the three kernels (M <= 4 vector-ALU
+    rows, M <= 16 split-K matrix cores, tiled GEMM above), K any multiple of
+    64 and of G up to about 20000 (so up to 20 segments of 1024 on the row
+    kernel), with and without bias."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.choice([32, 64, 128]))
+        step = max(64, G)
+        K = step * int(rng.integers(1, 20480 // step + 1))
+        N = int(rng.integers(1, 700))
+        M = int(rng.choice([1, 2, 3, 4, int(rng.integers(5, 17)), int(rng.integers(17, 200))]))
+        out.append((i, M, N, K, G, bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("i,M,N,K,G,bias", _random_cases())
+def test_w8a16_random_shapes(w4, i, M, N, K, G, bias):
+    run_linear(w4, M, N, K, G, bias=bias, seed=4000 + i)
+
+
 def test_w8a16_empty_batch(w4):
     q = torch.zeros((16, 128), dtype=torch.int8, device="cuda")
     s = torch.zeros((16, 4), dtype=torch.bfloat16, device="cuda")
