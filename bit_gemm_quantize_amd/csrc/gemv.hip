@@ -926,6 +926,10 @@ hipError_t allow_large_lds(Kern kern) {
 //     through LDS.
 constexpr int GV1_MAX_WAVES = 16;         // waves per block (1024 threads)
 constexpr int GV1_SEG = 2048;             // k per wave segment
+// segment waves per row group: a row spanning more segments gives each wave
+// every 8th (32768-wide rows: M = 1 and M = 2 13 % faster than one wave per
+// segment; the Llama-3-8B decode rows span at most 7)
+constexpr int GV1_SEG_WAVES = 8;
 
 // Sum over the 64 lanes of four row partials; every lane of quarter r ends
 // with row r's sum.
@@ -1137,7 +1141,7 @@ hipError_t launch_gemv1_mr(const uint16_t *x, const uint8_t *codes, const uint16
                            const uint16_t *zeros, const uint32_t *sz, const uint16_t *bias,
                            int N, int K, uint16_t *y, hipStream_t stream) {
     const int nseg = (K + GV1_SEG - 1) / GV1_SEG;
-    const int nsb = nseg < GV1_MAX_WAVES ? nseg : GV1_MAX_WAVES;
+    const int nsb = nseg < GV1_SEG_WAVES ? nseg : GV1_SEG_WAVES;
     const int rg = nsb >= 4 ? 1 : 4 / nsb;             // about four waves per block
     const bool xlds = nseg > 2;
     constexpr int R = 4;

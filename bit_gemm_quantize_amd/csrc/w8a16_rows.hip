@@ -17,8 +17,9 @@
 // row in v_dot2_f32_bf16; x (2 x 16 bytes per lane and activation row,
 // natural order) stays in registers for all R rows. (Against the split-K
 // matrix-core kernel, per Llama-3-8B decode layer: 15-40 % faster at M = 1
-// to 3, equal to 25 % faster at M = 4.) Scales: the segment's R x 1024/G values for the R rows come in one
-// or two loads per lane and reach the lanes of each group by lane permutes.
+// to 3, equal to 25 % faster at M = 4.) Scales: the segment's R x 1024/G
+// values for the R rows come in one or two loads per lane and reach the
+// lanes of each group by lane permutes.
 // The R partial sums are reduced across the wave with lane swaps and DPP,
 // then across the segment waves of a row group in LDS.
 #include "w4_device.h"
