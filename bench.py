@@ -51,7 +51,7 @@ KERNEL_SOURCES = {
     "gemm_kernel": ["gemm.hip", "w4_device.h"],
     "gemm_kernel_ps": ["gemm.hip", "w4_device.h"],
     "quantize8_kernel": ["w8a16.hip", "w4_device.h"],
-    "w8a16_gemv_rows_kernel": ["w8a16_rows.hip", "w4_device.h"],
+    "w8a16_gemv_rows_kernel": ["w8a16_rows.hip", "w4_rows.h", "w4_device.h"],
     "w8a16_gemm_kernel": ["w8a16.hip", "w4_device.h"],
     "w4a8_gemm_kernel": ["w4a8.hip", "w4_device.h"],
     "act_quant_kernel": ["w4a8.hip", "w4_device.h"],
@@ -702,6 +702,34 @@ def main():
 
     # ---- W4A8: per-token int8 activations + int4 weights on int8 MFMA -------
     if want("w4a8"):
+        # decode: M = 1 over the Llama-3-8B-shaped set (vector-ALU row kernel),
+        # each layer over >= 1 GiB of rotating copies in one graph
+        per = {}
+        tot_ms, tot_b = 0.0, 0
+        for li, (name, (N, K)) in enumerate(layers.items()):
+            b1 = N * K // 2 + 4 * N * K // G + K + 4 + 2 * N
+            n_l = max(2, -(-ROTATE_BYTES // b1))
+            W = make_weight(torch, N, K, 60 + li, dev)
+            c, s_, z = w4.quantize_int4_grouped(W, G)
+            del W
+            x8, sx = w4.quantize_act_int8(make_x(torch, 1, K, 660 + li, dev))
+            cps = [(c.clone(), s_.clone(), z.clone(), torch.empty((1, N), dtype=torch.bfloat16, device=dev))
+                   for _ in range(n_l)]
+            fns = [(lambda e=e: w4.w4a8_linear(x8, sx, e[0], e[1], e[2], G, out=e[3])) for e in cps]
+            for f_ in fns:
+                f_()
+            fns = fns * max(1, -(-64 // n_l))
+            g = graph_of(torch, fns)
+            ms = time_graphs(torch, [g], max(2, -(-reps // len(fns)))) / len(fns)
+            del g, fns, cps
+            per[name] = {"us": round(ms * 1e3, 3), "GBps": round(rate(b1, ms), 1)}
+            tot_ms += ms
+            tot_b += b1
+        out["w4a8_gemv_m1_g128"] = {
+            "kernel": "w4a8_gemv_rows_kernel<128, 1>", "bound": "hbm",
+            "avg_launch_us": round(tot_ms * 1e3 / len(layers), 3),
+            "achieved_GBps": round(rate(tot_b, tot_ms), 1),
+            "frac": round(rate(tot_b, tot_ms) / HBM_PEAK_GBS, 4), "per_layer": per}
         M = 2048
         for Gw in (128, 32):
             log(f"w4a8 G={Gw}: Gemma3-12B-shaped layers, M=2048")

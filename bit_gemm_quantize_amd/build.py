@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["abi.hip", "quantize.hip", "gemv.hip", "gemm.hip", "layout.hip", "w4a8.hip", "w8a16.hip",
-           "w8a16_rows.hip", "measure.hip"]
+           "w8a16_rows.hip", "w4a8_rows.hip", "measure.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

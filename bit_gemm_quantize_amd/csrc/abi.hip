@@ -186,8 +186,12 @@ w4_status w4a8_linear(const int8_t *x8, const float *sx, int64_t M, const uint8_
         overlap(y, ybytes, codes, N * K / 2) || overlap(y, ybytes, scales, gbytes) ||
         overlap(y, ybytes, zeros, gbytes) || overlap(y, ybytes, bias, 2 * N))
         return W4_ERR_ALIAS;
-    const hipError_t e = w4::launch_w4a8_gemm(x8, sx, M, codes, scales, zeros, bias, N, K,
-                                              static_cast<int>(G), y, stream);
+    const hipError_t e =
+        M <= w4::A8_ROWS_MAX_M && K <= w4::A8_ROWS_MAX_K
+            ? w4::launch_w4a8_rows(x8, sx, M, codes, scales, zeros, bias, N, K,
+                                   static_cast<int>(G), y, stream)
+            : w4::launch_w4a8_gemm(x8, sx, M, codes, scales, zeros, bias, N, K,
+                                   static_cast<int>(G), y, stream);
     return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
 

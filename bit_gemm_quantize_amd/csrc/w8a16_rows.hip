@@ -24,6 +24,7 @@
 // then across the segment waves of a row group in LDS.
 #include "w4_device.h"
 #include "w4_launch.h"
+#include "w4_rows.h"
 
 namespace w4 {
 
@@ -43,17 +44,6 @@ __device__ __forceinline__ void bytes4_to_bf16(uint32_t d, uint32_t &p01, uint32
     const float f2 = static_cast<float>((u >> 16) & 0xFFu), f3 = static_cast<float>(u >> 24);
     p01 = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
     p23 = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
-}
-
-// Sum over the 64 lanes of four row partials; every lane of quarter r ends
-// with row r's sum.
-__device__ __forceinline__ float sum_rows4(float v0, float v1, float v2, float v3) {
-    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v2), false, false);
-    const float u02 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v1), __float_as_uint(v3), false, false);
-    const float u13 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
-    auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(u02), __float_as_uint(u13), false, false);
-    return group_sum<16>(__uint_as_float(c[0]) + __uint_as_float(c[1]));
 }
 
 // A block holds rg row groups x nsb segment waves; a wave whose row needs
