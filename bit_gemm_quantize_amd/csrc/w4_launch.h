@@ -43,7 +43,7 @@ hipError_t launch_w4a8_gemm(const int8_t *x8, const float *sx, int64_t M, const 
 
 // Its decode kernel on the vector ALUs for 1 <= M <= A8_ROWS_MAX_M and
 // K <= A8_ROWS_MAX_K (32-bit buffer offsets); hipErrorInvalidValue otherwise.
-constexpr int64_t A8_ROWS_MAX_M = 4;
+constexpr int64_t A8_ROWS_MAX_M = 8;
 constexpr int64_t A8_ROWS_MAX_K = int64_t(1) << 24;
 hipError_t launch_w4a8_rows(const int8_t *x8, const float *sx, int64_t M, const uint8_t *codes,
                             const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,

@@ -1,4 +1,4 @@
-// W4A8 decode GEMV for one to four activation rows, on the vector ALUs
+// W4A8 decode GEMV for one to eight activation rows, on the vector ALUs
 // (gfx950).
 //
 // Same result as the W4A8 GEMM: per output, with the weights' q, s, z and
@@ -7,7 +7,7 @@
 //   P_g = sum_{k in g} x8[m][k] q[n][k],  X_g = sum_{k in g} x8[m][k]
 // with P and X exact int32 sums, the fold and the scale by sx in float32.
 //
-// At M <= 4 a 128-row matrix-core tile is almost all padding. Here a wave
+// At M <= 8 a 128-row matrix-core tile is almost all padding. Here a wave
 // takes R = 4 consecutive output rows and one 2048-wide K segment; lane l
 // covers k = 2048 s + 32 l .. + 32 (16 code bytes of each row, one 16-byte
 // load), so every code load of a row is 1 KB contiguous. A lane's 32 codes
@@ -38,7 +38,7 @@ __global__ __launch_bounds__(A8R_MAX_WAVES * 64) void w4a8_gemv_rows_kernel(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales,
     const uint16_t *__restrict__ zeros, const uint16_t *__restrict__ bias, int N, int K,
     uint16_t *__restrict__ y, int nseg, int nsb, int rg) {
-    static_assert(MR >= 1 && MR <= 4, "activation rows");
+    static_assert(MR >= 1 && MR <= A8_ROWS_MAX_M, "activation rows");
     constexpr int R = A8R_R;
     constexpr int GPS = A8R_SEG / G;              // groups per segment: 64, 32, 16
     constexpr int P = (R * GPS + 63) / 64;        // values per lane and array: 4, 2, 1
@@ -192,7 +192,11 @@ hipError_t launch_w4a8_rows(const int8_t *x8, const float *sx, int64_t M, const 
     case 1: return launch_rows<1>(x8, sx, codes, scales, zeros, bias, n, k, G, y, stream);
     case 2: return launch_rows<2>(x8, sx, codes, scales, zeros, bias, n, k, G, y, stream);
     case 3: return launch_rows<3>(x8, sx, codes, scales, zeros, bias, n, k, G, y, stream);
-    default: return launch_rows<4>(x8, sx, codes, scales, zeros, bias, n, k, G, y, stream);
+    case 4: return launch_rows<4>(x8, sx, codes, scales, zeros, bias, n, k, G, y, stream);
+    case 5: return launch_rows<5>(x8, sx, codes, scales, zeros, bias, n, k, G, y, stream);
+    case 6: return launch_rows<6>(x8, sx, codes, scales, zeros, bias, n, k, G, y, stream);
+    case 7: return launch_rows<7>(x8, sx, codes, scales, zeros, bias, n, k, G, y, stream);
+    default: return launch_rows<8>(x8, sx, codes, scales, zeros, bias, n, k, G, y, stream);
     }
 }
 

@@ -101,17 +101,18 @@ def run_case(w4, M, N, K, G, bias, seed, outliers=False):
                     (40, 96, 3840),
                     # fewer output rows than one 16-row tile, smallest K
                     (1, 1, 64), (3, 7, 64), (20, 15, 64),
-                    # M <= 4 on the vector-ALU kernel: 2048-wide segments, a
+                    # M <= 8 on the vector-ALU kernel: 2048-wide segments, a
                     # partial last one, more than 8 per row (a wave takes
-                    # several), even M with a bias
+                    # several)
                     (2, 33, 3840), (4, 19, 2048 + 64), (1, 40, 16384 + 2048), (3, 9, 20480),
-                    (4, 130, 4096)]
+                    (4, 130, 4096), (6, 33, 3840), (8, 19, 2048 + 64), (5, 40, 18432),
+                    (7, 130, 4096), (8, 9, 20480)]
     for G in (32, 64, 128) if K % G == 0])
 def test_w4a8_linear(w4, G, M, N, K):
     run_case(w4, M, N, K, G, bias=(M % 2 == 1), seed=7 * N + K + M + G)
 
 
-@pytest.mark.parametrize("M", [2, 4])
+@pytest.mark.parametrize("M", [2, 4, 6, 8])
 @pytest.mark.parametrize("G,N,K", [(32, 37, 2048), (128, 64, 4096), (64, 21, 14336)])
 def test_w4a8_even_rows_with_bias(w4, M, G, N, K):
     run_case(w4, M, N, K, G, bias=True, seed=9 * N + K + M)
