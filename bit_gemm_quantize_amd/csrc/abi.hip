@@ -32,6 +32,19 @@ w4_status check_nkg(int64_t N, int64_t K, int64_t G) {
     return W4_OK;
 }
 
+// M > 16 whose GEMM grid would leave most compute units idle: the decode
+// GEMV on ceil(M / 16) row slices reads the weight once per slice, but each
+// slice streams at close to the decode rate, while a GEMM of T 128 x 128 tiles
+// on C compute units runs at about T / C of its full rate. Measured on the
+// Llama-3-8B decode shapes (M = 17..128) the slices win while their count
+// stays below about 0.8 C / T; the rule keeps a margin (0.6 C / T).
+bool gemv_slices_pay(int64_t M, int64_t N, int64_t K) {
+    if (M <= W4_GEMV_MAX_M || K > W4_GEMV_MAX_K) return false;
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t slices = (M + W4_GEMV_MAX_M - 1) / W4_GEMV_MAX_M;
+    return 10 * slices * tiles <= 6 * static_cast<int64_t>(w4::compute_units());
+}
+
 // One implementation for both weight layouts: the plain one (scales and
 // zeros, sz == NULL) and the pre-shuffled one (sz, scales == zeros == NULL).
 w4_status linear_impl(const uint16_t *x, int64_t M, const uint8_t *codes,
@@ -60,6 +73,18 @@ w4_status linear_impl(const uint16_t *x, int64_t M, const uint8_t *codes,
 
     const bool gemv = path == W4_PATH_GEMV ||
                       (path == W4_PATH_AUTO && M <= W4_GEMV_MAX_M && K <= W4_GEMV_MAX_K);
+    if (!gemv && path == W4_PATH_AUTO && gemv_slices_pay(M, N, K)) {
+        // a few 16-row slices through the decode GEMV (each reads the weight
+        // once) instead of a GEMM grid too small to fill the chip
+        for (int64_t m0 = 0; m0 < M; m0 += W4_GEMV_MAX_M) {
+            const int64_t mc = M - m0 < W4_GEMV_MAX_M ? M - m0 : W4_GEMV_MAX_M;
+            const hipError_t e = w4::launch_gemv(x + m0 * K, static_cast<int>(mc), codes, scales,
+                                                 zeros, sz, bias, N, K, static_cast<int>(G),
+                                                 y + m0 * N, stream);
+            if (e != hipSuccess) return W4_ERR_HIP;
+        }
+        return W4_OK;
+    }
     const hipError_t e =
         gemv ? w4::launch_gemv(x, static_cast<int>(M), codes, scales, zeros, sz, bias, N, K,
                                static_cast<int>(G), y, stream)

@@ -61,7 +61,11 @@ typedef enum {
 } w4_status;
 
 /* Kernel selection for w4a16_linear_select. AUTO is what w4a16_linear does:
- * the decode GEMV for M <= 16, the prefill GEMM for M > 16. */
+ * the decode GEMV for M <= 16, the prefill GEMM for M > 16 - except when
+ * the GEMM's 128 x 128 tiles would be too few to fill the chip (ceil(M/16)
+ * x tiles <= 0.6 x compute units): then the decode GEMV runs on 16-row
+ * slices of x and y, one launch per slice. Results meet the same accuracy
+ * bound either way. */
 typedef enum {
     W4_PATH_AUTO = 0,
     W4_PATH_GEMV = 1,  /* valid for 1 <= M <= 16 */

@@ -145,6 +145,14 @@ def test_gemm_wide_blocks(w4, G, M, N, K):
     run_case(w4, M, N, K, G, bias=(N % 2 == 0), path=gu_path(w4, "GEMM"), seed=N + K + G)
 
 
+# M > 16 on a layer with few output tiles: AUTO runs the decode GEMV on
+# 16-row slices (a ragged last slice included, with and without bias).
+@pytest.mark.parametrize("M,N,K,G", [(17, 200, 4096, 128), (40, 300, 2048, 32),
+                                     (63, 130, 14336, 64), (100, 64, 1024, 128)])
+def test_auto_row_slices(w4, M, N, K, G):
+    run_case(w4, M, N, K, G, bias=(M % 2 == 1), path=gu_path(w4, "AUTO"), seed=17 * M + N + K)
+
+
 @pytest.mark.parametrize("M", [1, 16, 40, 300])
 @pytest.mark.parametrize("G", [32, 128])
 def test_auto_dispatch_outliers(w4, M, G):
