@@ -38,11 +38,14 @@ w4_status check_nkg(int64_t N, int64_t K, int64_t G) {
 // on C compute units runs at about T / C of its full rate. Measured on the
 // Llama-3-8B decode shapes (M = 17..128) the slices win while their count
 // stays below about 0.8 C / T; the rule keeps a margin (0.6 C / T).
+bool slices_pay(int64_t M, int64_t N, int64_t slice_rows) {
+    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    const int64_t slices = (M + slice_rows - 1) / slice_rows;
+    return 10 * slices * tiles <= 6 * static_cast<int64_t>(w4::compute_units());
+}
 bool gemv_slices_pay(int64_t M, int64_t N, int64_t K) {
     if (M <= W4_GEMV_MAX_M || K > W4_GEMV_MAX_K) return false;
-    const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    const int64_t slices = (M + W4_GEMV_MAX_M - 1) / W4_GEMV_MAX_M;
-    return 10 * slices * tiles <= 6 * static_cast<int64_t>(w4::compute_units());
+    return slices_pay(M, N, W4_GEMV_MAX_M);
 }
 
 // One implementation for both weight layouts: the plain one (scales and
@@ -211,12 +214,21 @@ w4_status w4a8_linear(const int8_t *x8, const float *sx, int64_t M, const uint8_
         overlap(y, ybytes, codes, N * K / 2) || overlap(y, ybytes, scales, gbytes) ||
         overlap(y, ybytes, zeros, gbytes) || overlap(y, ybytes, bias, 2 * N))
         return W4_ERR_ALIAS;
-    const hipError_t e =
-        M <= w4::A8_ROWS_MAX_M && K <= w4::A8_ROWS_MAX_K
-            ? w4::launch_w4a8_rows(x8, sx, M, codes, scales, zeros, bias, N, K,
-                                   static_cast<int>(G), y, stream)
-            : w4::launch_w4a8_gemm(x8, sx, M, codes, scales, zeros, bias, N, K,
-                                   static_cast<int>(G), y, stream);
+    if (K <= w4::A8_ROWS_MAX_K &&
+        (M <= w4::A8_ROWS_MAX_M || slices_pay(M, N, w4::A8_ROWS_MAX_M))) {
+        // the decode kernel, on slices of up to A8_ROWS_MAX_M rows when the
+        // GEMM's tiles would be too few to fill the chip (as for w4a16_linear)
+        for (int64_t m0 = 0; m0 < M; m0 += w4::A8_ROWS_MAX_M) {
+            const int64_t mc = M - m0 < w4::A8_ROWS_MAX_M ? M - m0 : w4::A8_ROWS_MAX_M;
+            const hipError_t e = w4::launch_w4a8_rows(x8 + m0 * K, sx + m0, mc, codes, scales,
+                                                      zeros, bias, N, K, static_cast<int>(G),
+                                                      y + m0 * N, stream);
+            if (e != hipSuccess) return W4_ERR_HIP;
+        }
+        return W4_OK;
+    }
+    const hipError_t e = w4::launch_w4a8_gemm(x8, sx, M, codes, scales, zeros, bias, N, K,
+                                              static_cast<int>(G), y, stream);
     return e == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
 

@@ -236,8 +236,10 @@ w4_status quantize_act_int8(const uint16_t *x, int64_t M, int64_t K, int8_t *x8,
  * P and X are exact int32 sums; the fold over groups, the scale by sx and
  * the bias are float32, then y is rounded to bf16 (nearest, ties to even).
  * Same weights (codes, scales, zeros) as w4a16_linear. With K <= 2^24,
- * M <= 8 runs a dot-product kernel on the vector ALUs (v_dot4_i32_i8);
- * every other M >= 1 the tiled int8-MFMA kernel. K must be a multiple of 64.
+ * M <= 8 runs a dot-product kernel on the vector ALUs (v_dot4_i32_i8), and
+ * so do 8-row slices of larger M while the tiled int8-MFMA kernel's
+ * 128 x 128 tiles would be too few to fill the chip (the rule of
+ * w4a16_linear); otherwise the tiled kernel. K must be a multiple of 64.
  *
  * x8, sx  in   from quantize_act_int8 (may be NULL when M == 0)
  * codes, scales, zeros, bias, N, K, G, y   as for w4a16_linear

@@ -112,6 +112,12 @@ def test_w4a8_linear(w4, G, M, N, K):
     run_case(w4, M, N, K, G, bias=(M % 2 == 1), seed=7 * N + K + M + G)
 
 
+# M > 8 on a layer with few output tiles: 8-row slices of the decode kernel
+@pytest.mark.parametrize("M,N,K,G", [(9, 200, 4096, 128), (16, 300, 2048, 32), (27, 130, 14336, 64)])
+def test_w4a8_row_slices(w4, M, N, K, G):
+    run_case(w4, M, N, K, G, bias=(M % 2 == 1), seed=19 * M + N + K)
+
+
 @pytest.mark.parametrize("M", [2, 4, 6, 8])
 @pytest.mark.parametrize("G,N,K", [(32, 37, 2048), (128, 64, 4096), (64, 21, 14336)])
 def test_w4a8_even_rows_with_bias(w4, M, G, N, K):
