@@ -304,11 +304,25 @@ w4_status w8a16_linear(const uint16_t *x, int64_t M, const int8_t *codes8,
     if (overlap(y, ybytes, x, 2 * M * K) || overlap(y, ybytes, codes8, N * K) ||
         overlap(y, ybytes, scales, 2 * N * (K / G)) || overlap(y, ybytes, bias, 2 * N))
         return W4_ERR_ALIAS;
-    const hipError_t e =
-        M <= w4::W8_ROWS_MAX_M && K <= w4::W8_ROWS_MAX_K
-            ? w4::launch_w8a16_rows(x, M, codes8, scales, bias, N, K, static_cast<int>(G), y, stream)
-            : w4::launch_w8a16(x, M, codes8, scales, bias, N, K, static_cast<int>(G), y, stream);
-    return e == hipSuccess ? W4_OK : W4_ERR_HIP;
+    // decode kernels: the vector-ALU rows for M <= W8_ROWS_MAX_M, the split-K
+    // matrix-core GEMV up to 16 rows (inside launch_w8a16)
+    auto decode = [&](const uint16_t *xs, int64_t mc, uint16_t *ys) {
+        return mc <= w4::W8_ROWS_MAX_M && K <= w4::W8_ROWS_MAX_K
+                   ? w4::launch_w8a16_rows(xs, mc, codes8, scales, bias, N, K,
+                                           static_cast<int>(G), ys, stream)
+                   : w4::launch_w8a16(xs, mc, codes8, scales, bias, N, K, static_cast<int>(G),
+                                      ys, stream);
+    };
+    if (M > W4_GEMV_MAX_M && K <= W4_GEMV_MAX_K && slices_pay(M, N, W4_GEMV_MAX_M)) {
+        // 16-row slices instead of a GEMM grid too small to fill the chip
+        // (the rule of w4a16_linear)
+        for (int64_t m0 = 0; m0 < M; m0 += W4_GEMV_MAX_M) {
+            const int64_t mc = M - m0 < W4_GEMV_MAX_M ? M - m0 : W4_GEMV_MAX_M;
+            if (decode(x + m0 * K, mc, y + m0 * N) != hipSuccess) return W4_ERR_HIP;
+        }
+        return W4_OK;
+    }
+    return decode(x, M, y) == hipSuccess ? W4_OK : W4_ERR_HIP;
 }
 
 const char *w4_status_string(int status) {

@@ -270,8 +270,10 @@ w4_status quantize_int8_grouped(const uint16_t *W, int64_t N, int64_t K, int64_t
  * w8a16_linear - y = x . w_hat^T (+ bias), w_hat = q * s (exact), each output
  * accumulated in float32 as sum_g s[n][g] * sum_{k in g} x[m][k] q[n][k] and
  * rounded to bf16. With K <= 2^24, M <= 4 runs a dot-product kernel on the
- * vector ALUs and 5 <= M <= 16 a split-K matrix-core kernel; other shapes a
- * tiled MFMA kernel. K must be a multiple of 64. Arguments as w4a16_linear
+ * vector ALUs and 5 <= M <= 16 a split-K matrix-core kernel, and so do
+ * 16-row slices of larger M while the tiled MFMA kernel's 128 x 128 tiles
+ * would be too few to fill the chip (the rule of w4a16_linear); other shapes
+ * the tiled MFMA kernel. K must be a multiple of 64. Arguments as w4a16_linear
  * with codes8 and scales from quantize_int8_grouped.
  */
 w4_status w8a16_linear(const uint16_t *x, int64_t M, const int8_t *codes8,

@@ -140,6 +140,13 @@ def test_w8a16_random_shapes(w4, i, M, N, K, G, bias):
     run_linear(w4, M, N, K, G, bias=bias, seed=4000 + i)
 
 
+# M > 16 on a layer with few output tiles: 16-row slices of the decode
+# kernels (a last slice of <= 4 rows on the vector-ALU kernel)
+@pytest.mark.parametrize("M,N,K,G", [(17, 200, 4096, 128), (35, 300, 2048, 32), (50, 130, 14336, 64)])
+def test_w8a16_row_slices(w4, M, N, K, G):
+    run_linear(w4, M, N, K, G, bias=(M % 2 == 1), seed=23 * M + N + K)
+
+
 def test_w8a16_empty_batch(w4):
     q = torch.zeros((16, 128), dtype=torch.int8, device="cuda")
     s = torch.zeros((16, 4), dtype=torch.bfloat16, device="cuda")
