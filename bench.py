@@ -54,6 +54,7 @@ KERNEL_SOURCES = {
     "w8a16_gemv_rows_kernel": ["w8a16_rows.hip", "w4_rows.h", "w4_device.h"],
     "w8a16_gemm_kernel": ["w8a16.hip", "w4_device.h"],
     "w4a8_gemm_kernel": ["w4a8.hip", "w4_device.h"],
+    "w4a8_gemv_rows_kernel": ["w4a8_rows.hip", "w4_rows.h", "w4_device.h"],
     "act_quant_kernel": ["w4a8.hip", "w4_device.h"],
     "read_stream_kernel": ["measure.hip", "w4_device.h"],
 }
@@ -869,6 +870,7 @@ def main():
                        ("w8a16_gemv_m1", "w8a16_gemv_rows_kernel"), ("quantize8_g128", "quantize8_kernel"),
                        ("w8a16_gemm_m2048", "w8a16_gemm_kernel"),
                        ("w4a8_gemm_m2048_g128", "w4a8_gemm_kernel"),
+                       ("w4a8_gemv_m1_g128", "w4a8_gemv_rows_kernel"),
                        ("gemv_m16_g32", "gemv_split_kernel_g32"),
                        ("gemv_m16_g64", "gemv_split_kernel_g64")):
         if comp in out:
